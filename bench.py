@@ -1,0 +1,309 @@
+#!/usr/bin/env python3
+"""Throughput of the FlashAttention forward and Flash-Decoding hot path on
+one MI355X.
+
+A step is one pass of the whole path over one batch of synthetic input:
+  1. fa_fwd on prefill_8k  (B=1, H=32, N=8192, d=128, bf16 N(0,1), non-causal)
+  2. fa_decode on decode_32k (B=1, H=32, L=32768, d=128, bf16 N(0,1), split-KV
+     + combine), reading one of four rotating KV caches so that the 512 MiB
+     cache is not served from the 256 MB last-level cache.
+Inputs are resident in HBM before timing starts.  W untimed warm-up steps,
+then exactly K timed steps between device synchronisations; each kernel is
+bracketed by HIP events on the stream it is launched on.
+
+Printed: one JSON line.  `value` is fa_fwd TFLOP/s on prefill_8k (algorithmic
+4*B*H*N^2*d FLOPs over the measured kernel time); decode GB/s (algorithmic
+K+V bytes over split+combine time) is reported beside it, together with the
+roofline fractions, the extra workloads (causal_4k, decode_varlen) and the
+float64 oracle timed on a bounded sample on the host cores.
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E, published
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_fwd_bf16_prefill_8k_traffic.json")
+KERNEL_SRC = os.path.join(ROOT, "exact_io_aware_02_amd", "csrc", "fa_fwd_bf16.hip")
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def _timed(fn, steps, warmup, torch):
+    """Run fn(i) warmup+steps times; returns the mean event time (ms) of the
+    timed calls, recorded on the current stream."""
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    evs = []
+    for i in range(steps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn(i)
+        b.record()
+        evs.append((a, b))
+    torch.cuda.synchronize()
+    return sum(a.elapsed_time(b) for a, b in evs) / steps
+
+
+def _traffic(n_launch_bytes_alg):
+    """Measured HBM bytes per fa_fwd launch from committed rocprofv3 counters,
+    valid only while the kernel source is unchanged."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        t = json.load(f)
+    src = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+    if t.get("kernel_sha256") != src:
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(Q, K, V, seconds, torch):
+    """The float64 oracle, as it stands, on whole heads of prefill_8k until
+    about `seconds` of host time is spent (at least one head)."""
+    import numpy as np
+
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    B, H, N, d = Q.shape
+    flops = 0.0
+    spent = 0.0
+    heads = 0
+    for h in range(H):
+        q, k, v = (t[0, h].float().cpu().numpy().astype(np.float64) for t in (Q, K, V))
+        t0 = time.perf_counter()
+        oracle.attention_rows(q, k, v, 1 / math.sqrt(d), causal=False)
+        spent += time.perf_counter() - t0
+        flops += 4.0 * N * N * d
+        heads += 1
+        if spent >= seconds:
+            break
+    return {
+        "value": flops / spent / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(cores),
+        "kind": "oracle",
+        "sample": f"{heads} of {H} heads of prefill_8k (all {N} query rows each), float64 numpy",
+        "seconds": round(spent, 3),
+    }
+
+
+def parity_sample(Q, K, V, O, L, q, Kc, Vc, o, lengths, torch):
+    import numpy as np
+
+    import oracle
+
+    N, d = Q.shape[2], Q.shape[3]
+    rows = np.array([0, 1, 127, 128, 4095, 8190, 8191])
+    dO = dL = 0.0
+    for h in (0, 31):
+        f = lambda t: t.float().cpu().numpy().astype(np.float64)
+        o_ref, l_ref = oracle.attention_rows(f(Q[0, h, rows]), f(K[0, h]), f(V[0, h]), 1 / math.sqrt(d), q_pos=rows)
+        dO = max(dO, float(np.abs(f(O[0, h, rows]) - o_ref).max()))
+        dL = max(dL, float(np.abs(f(L[0, h, rows]) - l_ref).max()))
+    Ld = int(lengths[0])
+    dd = 0.0
+    for h in (0, 31):
+        k = Kc[0, h].float().cpu().numpy().astype(np.float64)
+        v = Vc[0, h].float().cpu().numpy().astype(np.float64)
+        o_ref, _ = oracle.decode_ref(q[0, h].float().cpu().numpy().astype(np.float64), k[:Ld], v[:Ld], 1 / math.sqrt(d))
+        dd = max(dd, float(np.abs(o[0, h].float().cpu().numpy() - o_ref).max()))
+    return {"prefill_8k_max_abs_dO": dO, "prefill_8k_max_abs_dL": dL, "decode_32k_max_abs_do": dd,
+            "rows_checked": "prefill: 7 rows x 2 heads; decode: 2 heads"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="host time budget of the oracle baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip causal_4k and decode_varlen")
+    ap.add_argument("--num-splits", type=int, default=0, help="decode splits (0 = automatic)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(
+            "bench.py measures one GPU: the FlashAttention forward and Flash-Decoding kernels "
+            "run on a single MI355X here; multi-GPU runs are not part of this library "
+            "(see DESIGN.md for how the path would shard).",
+            file=sys.stderr,
+        )
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import exact_io_aware_02_amd as fa
+    import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    dev = "cuda"
+    K_, W_ = args.steps, args.warmup
+
+    # ---------------- inputs (resident in HBM before timing)
+    cfg = synth.WORKLOADS["prefill_8k"]
+    B, H, N, d = cfg["B"], cfg["H"], cfg["N"], cfg["d"]
+    Q, K, V = synth.prefill_inputs("prefill_8k", dev)
+    O = torch.empty_like(Q)
+    L = torch.empty(B, H, N, device=dev)
+    scale = 1 / math.sqrt(d)
+
+    dcfg = synth.WORKLOADS["decode_32k"]
+    n_rot = 4
+    caches = [synth.decode_inputs("decode_32k", dev, seed_offset=r) for r in range(n_rot)]
+    lengths = caches[0][3]
+    Lkv = torch.tensor(lengths, dtype=torch.int32, device=dev)
+    Bd, Hd, dd = dcfg["B"], dcfg["H"], dcfg["d"]
+    od = torch.empty(Bd, Hd, dd, dtype=torch.bfloat16, device=dev)
+    splits = args.num_splits
+    torch.cuda.synchronize()
+    log("inputs ready")
+
+    def run_fwd(i):
+        fa.fa_fwd(Q, K, V, O, L, causal=False, scale=scale)
+
+    def run_dec(i):
+        q, Kc, Vc, _ = caches[i % n_rot]
+        fa.fa_decode(q, Kc, Vc, od, Lkv, num_splits=splits)
+
+    # ---------------- the timed steps
+    for i in range(W_):
+        run_fwd(i)
+        run_dec(i)
+    torch.cuda.synchronize()
+    evs = []
+    t0 = time.perf_counter()
+    for i in range(K_):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        e[0].record()
+        run_fwd(i)
+        e[1].record()
+        run_dec(i)
+        e[2].record()
+        evs.append(e)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / K_
+    fwd_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / K_
+    dec_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / K_
+    log(f"fa_fwd {fwd_ms:.4f} ms, fa_decode {dec_ms * 1e3:.2f} us, wall/step {wall_ms:.4f} ms")
+
+    flops = 4.0 * B * H * N * N * d
+    tflops = flops / (fwd_ms * 1e-3) / 1e12
+    dec_bytes = 2.0 * Bd * Hd * int(lengths[0]) * dd * 2
+    dec_gbs = dec_bytes / (dec_ms * 1e-3) / 1e9
+    plan = fa.fa_fwd_plan(B, H, N, d, 0)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+
+    result = {
+        "metric": "fa_fwd TFLOP/s (% MFMA peak) at N=8192,d=128; decode GB/s (% HBM peak) L=32k",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K_,
+        "warmup": W_,
+        "ms_per_step": round(wall_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded N(0,1) bf16 tensors of the workload shapes",
+        "config": {
+            "workload": "prefill_8k (B=1,H=32,N=8192,d=128, non-causal) + decode_32k (B=1,H=32,L=32768,d=128)",
+            "prefill": {"B": B, "H": H, "N": N, "d": d, "causal": False,
+                        "block_rows": plan["block_rows"], "block_cols": plan["block_cols"],
+                        "workgroups": plan["workgroups"]},
+            "decode": {"B": Bd, "H": Hd, "L": int(lengths[0]), "d": dd,
+                       "num_splits": splits if splits else f"auto ({cus} CUs)", "rotating_caches": n_rot},
+        },
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(tflops, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": _traffic(None),
+            "kernel": "fwd_bf16_kernel<128,false>",
+            "ms_per_launch": round(fwd_ms, 5),
+        },
+        "decode": {
+            "value": round(dec_gbs, 1),
+            "unit": "GB/s",
+            "us_per_step": round(dec_ms * 1e3, 2),
+            "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": round(dec_gbs / PEAK_HBM_GBS, 4),
+                         "bytes_per_step": dec_bytes},
+        },
+    }
+
+    # ---------------- extra workloads (the causal target and varlen decode)
+    if not args.no_extra:
+        c3 = synth.WORKLOADS["causal_4k"]
+        Qc, Kc3, Vc3 = synth.prefill_inputs("causal_4k", dev)
+        Oc = torch.empty_like(Qc)
+        Lc = torch.empty(Qc.shape[:3], device=dev)
+        ms_c = _timed(lambda i: fa.fa_fwd(Qc, Kc3, Vc3, Oc, Lc, causal=True), K_, W_, torch)
+        Bc, Hc, Nc, dc = c3["B"], c3["H"], c3["N"], c3["d"]
+        alg = 4.0 * dc * Bc * Hc * Nc * (Nc + 1) / 2
+        pc = fa.fa_fwd_plan(Bc, Hc, Nc, dc, 1)
+        executed = 4.0 * pc["tiles_visited"] * pc["block_rows"] * pc["block_cols"] * dc
+        tf_c = alg / (ms_c * 1e-3) / 1e12
+        result["causal_4k"] = {
+            "value": round(tf_c, 2), "unit": "TFLOP/s", "ms_per_launch": round(ms_c, 5),
+            "frac_of_peak": round(tf_c / PEAK_BF16_TFLOPS, 4),
+            "flops_algorithmic": alg, "flops_executed_tiles": executed,
+        }
+        del Qc, Kc3, Vc3, Oc, Lc
+        log(f"causal_4k {ms_c:.4f} ms -> {tf_c:.1f} TFLOP/s")
+
+        qv, Kv, Vv, lv = synth.decode_inputs("decode_varlen", dev)
+        Lv = torch.tensor(lv, dtype=torch.int32, device=dev)
+        ov = torch.empty_like(qv)
+        ms_v = _timed(lambda i: fa.fa_decode(qv, Kv, Vv, ov, Lv, num_splits=splits), K_, W_, torch)
+        vbytes = 2.0 * qv.shape[1] * qv.shape[2] * 2 * int(lv.sum())
+        gbs_v = vbytes / (ms_v * 1e-3) / 1e9
+        result["decode_varlen"] = {
+            "value": round(gbs_v, 1), "unit": "GB/s", "us_per_launch": round(ms_v * 1e3, 2),
+            "frac_of_peak": round(gbs_v / PEAK_HBM_GBS, 4), "bytes": vbytes,
+            "lengths": [int(x) for x in lv],
+        }
+        del qv, Kv, Vv, ov
+        log(f"decode_varlen {ms_v * 1e3:.1f} us -> {gbs_v:.1f} GB/s")
+
+    # ---------------- light parity check of the timed outputs
+    q0, Kc0, Vc0, _ = caches[(K_ - 1) % n_rot]
+    fa.fa_decode(q0, Kc0, Vc0, od, Lkv, num_splits=splits)
+    torch.cuda.synchronize()
+    result["parity_sample"] = parity_sample(
+        Q, K, V, O, L, q0, Kc0.view(Bd, Hd, -1, dd), Vc0.view(Bd, Hd, -1, dd), od, lengths, torch)
+
+    # ---------------- float64 oracle on the host cores
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(Q, K, V, args.cpu_seconds, torch)
+        log(f"cpu baseline {result['cpu_baseline']}")
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

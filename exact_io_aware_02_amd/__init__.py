@@ -1,0 +1,31 @@
+"""Exact attention forward (FlashAttention) and Flash-Decoding for AMD
+MI355X (gfx950).
+
+The compute lives in libfa.so (HIP kernels behind the C ABI of include/fa.h);
+this package is its ctypes binding.  Build the library in-tree with
+`python -m exact_io_aware_02_amd.build`.
+"""
+
+from ._binding import (  # noqa: F401
+    EXPORTED,
+    FAError,
+    FA_OK,
+    FA_ERR_INVALID_ARG,
+    FA_ERR_UNSUPPORTED,
+    FA_ERR_HIP,
+    FA_ERR_NOMEM,
+    FA_ERR_WORKSPACE,
+    LIB_PATH,
+    fa_decode,
+    fa_decode_chunk_tokens,
+    fa_decode_ex,
+    fa_decode_plan,
+    fa_decode_workspace_bytes,
+    fa_fwd,
+    fa_fwd_f32,
+    fa_fwd_plan,
+    fa_release_workspace,
+    last_error,
+    lib,
+    status_string,
+)

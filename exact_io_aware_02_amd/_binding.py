@@ -1,0 +1,244 @@
+"""ctypes binding of libfa.so: argument marshalling only.
+
+Every computation runs in the HIP kernels behind the C ABI declared in
+include/fa.h.  The raw entry points take integer device pointers exactly like
+the C functions; the tensor-taking wrappers of the same names read shapes,
+data pointers and the current stream from torch tensors and call them.  There
+is no fallback: if libfa.so is missing, importing this module fails.
+"""
+
+import ctypes
+import math
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfa.so")
+
+FA_OK = 0
+FA_ERR_INVALID_ARG = -1
+FA_ERR_UNSUPPORTED = -2
+FA_ERR_HIP = -3
+FA_ERR_NOMEM = -4
+FA_ERR_WORKSPACE = -5
+
+
+class FAError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"{message} (status {status})")
+        self.status = status
+
+
+class fa_fwd_plan_t(ctypes.Structure):
+    _fields_ = [
+        ("block_rows", ctypes.c_int),
+        ("block_cols", ctypes.c_int),
+        ("q_tiles", ctypes.c_int),
+        ("kv_tiles", ctypes.c_int),
+        ("threads_per_workgroup", ctypes.c_int),
+        ("lds_bytes", ctypes.c_int),
+        ("workgroups", ctypes.c_int64),
+        ("tiles_visited", ctypes.c_int64),
+        ("tiles_masked", ctypes.c_int64),
+    ]
+
+
+class fa_decode_plan_t(ctypes.Structure):
+    _fields_ = [
+        ("num_splits", ctypes.c_int),
+        ("threads_per_workgroup", ctypes.c_int),
+        ("split_workgroups", ctypes.c_int64),
+        ("combine_workgroups", ctypes.c_int64),
+        ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with `python -m exact_io_aware_02_amd.build` "
+            "(or __graft_entry__.build()); there is no non-HIP fallback"
+        )
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I, F, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    sig = {
+        "fa_fwd": (I, [P, P, P, P, P, I, I, I, I, I, F, P]),
+        "fa_fwd_f32": (I, [P, P, P, P, P, I, I, I, I, I, F, P]),
+        "fa_decode": (I, [P, P, P, P, I, I, P, I, I, P]),
+        "fa_decode_ex": (I, [P, P, P, P, P, I, I, P, I, I, I, F, P, Z, P]),
+        "fa_decode_workspace_bytes": (Z, [I, I, I, I]),
+        "fa_fwd_plan": (I, [I, I, I, I, I, ctypes.POINTER(fa_fwd_plan_t)]),
+        "fa_decode_plan": (I, [I, I, I, I, ctypes.POINTER(fa_decode_plan_t)]),
+        "fa_decode_chunk_tokens": (I, [I, I]),
+        "fa_release_workspace": (I, []),
+        "fa_status_string": (ctypes.c_char_p, [I]),
+        "fa_last_error": (ctypes.c_char_p, []),
+        "fa_version": (I, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+lib = _load()
+
+# names of every symbol include/fa.h declares
+EXPORTED = (
+    "fa_fwd",
+    "fa_fwd_f32",
+    "fa_decode",
+    "fa_decode_ex",
+    "fa_decode_workspace_bytes",
+    "fa_fwd_plan",
+    "fa_decode_plan",
+    "fa_decode_chunk_tokens",
+    "fa_release_workspace",
+    "fa_status_string",
+    "fa_last_error",
+    "fa_version",
+)
+
+
+def _check(status):
+    if status != FA_OK:
+        msg = lib.fa_last_error().decode() or lib.fa_status_string(status).decode()
+        raise FAError(status, msg)
+    return status
+
+
+def last_error():
+    return lib.fa_last_error().decode()
+
+
+def status_string(status):
+    return lib.fa_status_string(status).decode()
+
+
+# --------------------------------------------------------------------------
+# host-only planning
+# --------------------------------------------------------------------------
+
+def fa_fwd_plan(B, H, N, d, causal):
+    p = fa_fwd_plan_t()
+    _check(lib.fa_fwd_plan(B, H, N, d, int(causal), ctypes.byref(p)))
+    return {f: getattr(p, f) for f, _ in fa_fwd_plan_t._fields_}
+
+
+def fa_decode_plan(B, H, d, num_splits=0):
+    p = fa_decode_plan_t()
+    _check(lib.fa_decode_plan(B, H, d, num_splits, ctypes.byref(p)))
+    return {f: getattr(p, f) for f, _ in fa_decode_plan_t._fields_}
+
+
+def fa_decode_chunk_tokens(kv_len, num_splits):
+    return lib.fa_decode_chunk_tokens(int(kv_len), int(num_splits))
+
+
+def fa_decode_workspace_bytes(B, H, d, num_splits=0):
+    return lib.fa_decode_workspace_bytes(B, H, d, num_splits)
+
+
+def fa_release_workspace():
+    _check(lib.fa_release_workspace())
+
+
+# --------------------------------------------------------------------------
+# tensor wrappers (torch is used for device memory and the stream only)
+# --------------------------------------------------------------------------
+
+def _stream_ptr(stream):
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _expect(t, dtype, shape, name):
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor")
+
+
+def fa_fwd(Q, K, V, O, L=None, causal=False, scale=None, stream=None):
+    """O = softmax(Q K^T * scale) V for bf16 [B, H, N, d]; L (fp32 [B, H, N])
+    receives the per-row log-sum-exp if given."""
+    import torch
+
+    B, H, N, d = Q.shape
+    for t, n in ((Q, "Q"), (K, "K"), (V, "V"), (O, "O")):
+        _expect(t, torch.bfloat16, (B, H, N, d), n)
+    if L is not None:
+        _expect(L, torch.float32, (B, H, N), "L")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    _check(lib.fa_fwd(_ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(L), B, H, N, d, int(causal),
+                      float(scale), _stream_ptr(stream)))
+    return O, L
+
+
+def fa_fwd_f32(Q, K, V, O, L=None, causal=False, scale=None, stream=None):
+    """fp32 variant of fa_fwd: Q, K, V, O fp32 [B, H, N, d]."""
+    import torch
+
+    B, H, N, d = Q.shape
+    for t, n in ((Q, "Q"), (K, "K"), (V, "V"), (O, "O")):
+        _expect(t, torch.float32, (B, H, N, d), n)
+    if L is not None:
+        _expect(L, torch.float32, (B, H, N), "L")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    _check(lib.fa_fwd_f32(_ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(L), B, H, N, d, int(causal),
+                          float(scale), _stream_ptr(stream)))
+    return O, L
+
+
+def _decode_shapes(q, Kcache, Vcache, o, Lkv):
+    import torch
+
+    B, H, d = q.shape
+    _expect(q, torch.bfloat16, (B, H, d), "q")
+    _expect(o, torch.bfloat16, (B, H, d), "o")
+    _expect(Lkv, torch.int32, (B,), "Lkv")
+    for t, n in ((Kcache, "Kcache"), (Vcache, "Vcache")):
+        if t.dtype != torch.bfloat16 or not t.is_contiguous() or t.device.type != "cuda":
+            raise ValueError(f"{n} must be a contiguous bf16 device tensor")
+    return B, H, d
+
+
+def fa_decode(q, Kcache, Vcache, o, Lkv, num_splits=0, stream=None):
+    """Flash-Decoding: q, o bf16 [B, H, d]; Kcache/Vcache packed bf16 caches;
+    Lkv int32 [B] device lengths.  Uses the library's internal workspace."""
+    B, H, d = _decode_shapes(q, Kcache, Vcache, o, Lkv)
+    _check(lib.fa_decode(_ptr(q), _ptr(Kcache), _ptr(Vcache), _ptr(o), B, H, _ptr(Lkv), d,
+                         int(num_splits), _stream_ptr(stream)))
+    return o
+
+
+def fa_decode_ex(q, Kcache, Vcache, o, Lkv, workspace, lse_out=None, kv_seq_capacity=0,
+                 num_splits=0, scale=None, stream=None):
+    """fa_decode with a caller-owned workspace (a device tensor of at least
+    fa_decode_workspace_bytes(...) bytes), optional lse_out fp32 [B, H] and
+    the padded layout when kv_seq_capacity > 0."""
+    import torch
+
+    B, H, d = _decode_shapes(q, Kcache, Vcache, o, Lkv)
+    if lse_out is not None:
+        _expect(lse_out, torch.float32, (B, H), "lse_out")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(lib.fa_decode_ex(_ptr(q), _ptr(Kcache), _ptr(Vcache), _ptr(o), _ptr(lse_out), B, H,
+                            _ptr(Lkv), int(kv_seq_capacity), d, int(num_splits), float(scale),
+                            _ptr(workspace), nbytes, _stream_ptr(stream)))
+    return o, lse_out

@@ -1,0 +1,83 @@
+"""Build libfa.so (the HIP kernels and the C ABI) in-tree for gfx950.
+
+    python -m exact_io_aware_02_amd.build [--verbose]
+
+Every source is compiled on each call (hipcc cross-compiles without a GPU).
+"""
+
+import argparse
+import os
+import shutil
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+OBJDIR = os.path.join(PKG, "_build")
+LIB = os.path.join(PKG, "libfa.so")
+
+SOURCES = ["fa_api.hip", "fa_fwd_bf16.hip", "fa_fwd_f32.hip", "fa_decode.hip"]
+
+ARCH = "gfx950"
+# -packed-fp32-ops: keep the compiler from forming v_pk_{add,mul,fma}_f32
+# (the host pass prints a harmless "not a recognized feature" warning).
+FLAGS = [
+    f"--offload-arch={ARCH}",
+    "-O3",
+    "-std=c++17",
+    "-fPIC",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-I", INCLUDE,
+    "-I", CSRC,
+]
+
+
+def _hipcc():
+    exe = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(exe):
+        raise RuntimeError("hipcc not found (ROCm is required to build libfa.so)")
+    return exe
+
+
+def _run(cmd, verbose):
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    p = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    out = "\n".join(
+        ln for ln in p.stdout.splitlines() if "packed-fp32-ops' is not a recognized feature" not in ln
+    )
+    if p.returncode != 0:
+        raise RuntimeError(f"build failed: {' '.join(cmd)}\n{out}")
+    if verbose and out.strip():
+        print(out, flush=True)
+
+
+def build(verbose=False, resource_usage=False):
+    """Compile every source and link libfa.so; returns its path."""
+    os.makedirs(OBJDIR, exist_ok=True)
+    hipcc = _hipcc()
+    extra = ["-Rpass-analysis=kernel-resource-usage"] if resource_usage else []
+    objs = []
+    cmds = []
+    for src in SOURCES:
+        obj = os.path.join(OBJDIR, src.replace(".hip", ".o"))
+        objs.append(obj)
+        cmds.append([hipcc, *FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj])
+    with ThreadPoolExecutor(max_workers=min(4, len(cmds))) as ex:
+        list(ex.map(lambda c: _run(c, verbose or resource_usage), cmds))
+    tmp = LIB + ".tmp"
+    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--verbose", action="store_true")
+    ap.add_argument("--resource-usage", action="store_true", help="print VGPR/LDS usage per kernel")
+    a = ap.parse_args()
+    print(build(verbose=a.verbose, resource_usage=a.resource_usage))
+    sys.exit(0)

@@ -1,0 +1,342 @@
+// C-ABI entry points: argument validation (before any HIP call), launch
+// planning, decode workspace management, and error reporting.
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <map>
+#include <mutex>
+#include <string>
+#include <utility>
+
+#include "fa.h"
+#include "fa_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+int ok() { return FA_OK; }
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(FA_ERR_HIP, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  if (a == nullptr || b == nullptr || na == 0 || nb == 0) return false;
+  uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+  return a0 < b0 + nb && b0 < a0 + na;
+}
+
+// Common prefill checks.  elem = bytes per element of Q/K/V/O.
+int check_fwd(const void* Q, const void* K, const void* V, const void* O, const float* L, int B,
+              int H, int N, int d, int causal, float scale, size_t elem, int rows_per_wg) {
+  if (!Q || !K || !V || !O) return fail(FA_ERR_INVALID_ARG, "null tensor pointer");
+  if (B < 1 || H < 1 || N < 1) return fail(FA_ERR_INVALID_ARG, "B, H, N must be >= 1 (got %d, %d, %d)", B, H, N);
+  if (d < 1) return fail(FA_ERR_INVALID_ARG, "d must be >= 1 (got %d)", d);
+  if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "head dimension %d not supported (64 or 128)", d);
+  if (causal != 0 && causal != 1) return fail(FA_ERR_INVALID_ARG, "causal must be 0 or 1 (got %d)", causal);
+  if (!(isfinite(scale) && scale > 0.f)) return fail(FA_ERR_INVALID_ARG, "scale must be finite and > 0");
+  if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16))
+    return fail(FA_ERR_INVALID_ARG, "Q, K, V, O must be 16-byte aligned");
+  if (L && !aligned(L, 4)) return fail(FA_ERR_INVALID_ARG, "L must be 4-byte aligned");
+  const int64_t q_tiles = fa::ceil_div64(N, rows_per_wg);
+  if ((int64_t)B * H * q_tiles > 0x7fffffffLL) return fail(FA_ERR_INVALID_ARG, "grid too large");
+  if ((int64_t)N > (1LL << 30)) return fail(FA_ERR_INVALID_ARG, "N too large");
+  const size_t tbytes = (size_t)B * H * N * d * elem;
+  const size_t lbytes = L ? (size_t)B * H * N * sizeof(float) : 0;
+  if (overlap(O, tbytes, Q, tbytes) || overlap(O, tbytes, K, tbytes) || overlap(O, tbytes, V, tbytes))
+    return fail(FA_ERR_INVALID_ARG, "O overlaps an input");
+  if (overlap(L, lbytes, Q, tbytes) || overlap(L, lbytes, K, tbytes) || overlap(L, lbytes, V, tbytes) ||
+      overlap(L, lbytes, O, tbytes))
+    return fail(FA_ERR_INVALID_ARG, "L overlaps another tensor");
+  return FA_OK;
+}
+
+int check_decode(const void* q, const void* Kc, const void* Vc, const void* o, const float* lse,
+                 int B, int H, const int32_t* Lkv, int cap, int d, int num_splits, float scale) {
+  if (!q || !Kc || !Vc || !o || !Lkv) return fail(FA_ERR_INVALID_ARG, "null pointer argument");
+  if (B < 1 || H < 1) return fail(FA_ERR_INVALID_ARG, "B, H must be >= 1 (got %d, %d)", B, H);
+  if (B > 65535 || H > 65535) return fail(FA_ERR_INVALID_ARG, "B and H must be <= 65535");
+  if (d < 1) return fail(FA_ERR_INVALID_ARG, "d must be >= 1 (got %d)", d);
+  if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "head dimension %d not supported (64 or 128)", d);
+  if (num_splits < 0 || num_splits > 4096) return fail(FA_ERR_INVALID_ARG, "num_splits must be in [0, 4096]");
+  if (cap < 0) return fail(FA_ERR_INVALID_ARG, "kv_seq_capacity must be >= 0");
+  if (!(isfinite(scale) && scale > 0.f)) return fail(FA_ERR_INVALID_ARG, "scale must be finite and > 0");
+  if (!aligned(q, 16) || !aligned(Kc, 16) || !aligned(Vc, 16) || !aligned(o, 16))
+    return fail(FA_ERR_INVALID_ARG, "q, Kcache, Vcache, o must be 16-byte aligned");
+  if (!aligned(Lkv, 4) || (lse && !aligned(lse, 4))) return fail(FA_ERR_INVALID_ARG, "Lkv/lse_out misaligned");
+  const size_t ob = (size_t)B * H * d * 2, lb = lse ? (size_t)B * H * 4 : 0;
+  if (overlap(o, ob, q, ob) || overlap(o, ob, Kc, 1) || overlap(o, ob, Vc, 1) || overlap(o, ob, Lkv, (size_t)B * 4))
+    return fail(FA_ERR_INVALID_ARG, "o overlaps an input");
+  if (overlap(lse, lb, o, ob) || overlap(lse, lb, q, ob) || overlap(lse, lb, Lkv, (size_t)B * 4))
+    return fail(FA_ERR_INVALID_ARG, "lse_out overlaps another buffer");
+  return FA_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t ws_bytes(int B, int H, int d, int S) {
+  const size_t parts = (size_t)B * H * S;
+  return align256(parts * d * sizeof(float)) + align256(parts * sizeof(float));
+}
+
+// Compute-unit count per device, queried once.
+int cu_count(int* out) {
+  static std::mutex mu;
+  static std::map<int, int> cache;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  std::lock_guard<std::mutex> lk(mu);
+  auto it = cache.find(dev);
+  if (it == cache.end()) {
+    int cus = 0;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
+    it = cache.emplace(dev, cus).first;
+  }
+  *out = it->second;
+  return FA_OK;
+}
+
+// Automatic split count: enough workgroups for about eight per compute unit.
+int auto_splits(int B, int H, int cus) {
+  const int64_t bh = (int64_t)B * H;
+  int64_t s = fa::ceil_div64(8LL * cus, bh);
+  if (s < 1) s = 1;
+  if (s > 256) s = 256;
+  return (int)s;
+}
+
+struct Workspace {
+  void* ptr = nullptr;
+  size_t bytes = 0;
+};
+std::mutex g_ws_mu;
+std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+
+int decode_common(const void* q, const void* Kc, const void* Vc, void* o, float* lse, int B, int H,
+                  const int32_t* Lkv, int cap, int d, int S, float scale, void* ws, hipStream_t st) {
+  fa::DecodeArgs a;
+  a.q = q;
+  a.K = Kc;
+  a.V = Vc;
+  a.o = o;
+  a.lse_out = lse;
+  a.Lkv = Lkv;
+  const size_t parts = (size_t)B * H * S;
+  a.part_o = static_cast<float*>(ws);
+  a.part_lse = reinterpret_cast<float*>(static_cast<char*>(ws) + align256(parts * d * sizeof(float)));
+  a.B = B;
+  a.H = H;
+  a.S = S;
+  a.capacity = cap;
+  a.scale = scale;
+  hipError_t e = fa::launch_decode(a, d, st);
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fa_status_string(int status) {
+  switch (status) {
+    case FA_OK: return "ok";
+    case FA_ERR_INVALID_ARG: return "invalid argument";
+    case FA_ERR_UNSUPPORTED: return "unsupported";
+    case FA_ERR_HIP: return "HIP error";
+    case FA_ERR_NOMEM: return "out of device memory";
+    case FA_ERR_WORKSPACE: return "workspace missing or too small";
+    default: return "unknown status";
+  }
+}
+
+const char* fa_last_error(void) { return g_last_error.c_str(); }
+
+int fa_version(void) { return (1 << 16) | 0; }
+
+int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* L, int B, int H, int N,
+           int d, int causal, float scale, void* stream) {
+  int st = check_fwd(Q, K, V, O, L, B, H, N, d, causal, scale, 2, fa::kFwdBR);
+  if (st != FA_OK) return st;
+  fa::FwdArgs a{Q, K, V, O, L, B, H, N, causal, scale};
+  hipError_t e = fa::launch_fwd_bf16(a, d, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "fa_fwd launch");
+  return ok();
+}
+
+int fa_fwd_f32(const float* Q, const float* K, const float* V, float* O, float* L, int B, int H,
+               int N, int d, int causal, float scale, void* stream) {
+  int st = check_fwd(Q, K, V, O, L, B, H, N, d, causal, scale, 4, fa::kF32BR);
+  if (st != FA_OK) return st;
+  fa::FwdArgs a{Q, K, V, O, L, B, H, N, causal, scale};
+  hipError_t e = fa::launch_fwd_f32(a, d, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "fa_fwd_f32 launch");
+  return ok();
+}
+
+int fa_fwd_plan(int B, int H, int N, int d, int causal, fa_fwd_plan_t* out) {
+  if (!out) return fail(FA_ERR_INVALID_ARG, "null plan pointer");
+  if (B < 1 || H < 1 || N < 1) return fail(FA_ERR_INVALID_ARG, "B, H, N must be >= 1");
+  if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "head dimension %d not supported", d);
+  if (causal != 0 && causal != 1) return fail(FA_ERR_INVALID_ARG, "causal must be 0 or 1");
+  const int q_tiles = (int)fa::ceil_div64(N, fa::kFwdBR);
+  out->block_rows = fa::kFwdBR;
+  out->block_cols = fa::kFwdBC;
+  out->q_tiles = q_tiles;
+  out->kv_tiles = (int)fa::ceil_div64(N, fa::kFwdBC);
+  out->threads_per_workgroup = fa::kFwdWaves * 64;
+  out->lds_bytes = 2 * (fa::kFwdBC * d * 2 + d * fa::kFwdBC * 2);
+  out->workgroups = (int64_t)B * H * q_tiles;
+  int64_t visited = 0, masked = 0;
+  for (int qt = 0; qt < q_tiles; ++qt) {
+    const int n = fa::fwd_kv_tiles_for(qt, N, causal);
+    visited += n;
+    for (int j = 0; j < n; ++j) {
+      const int kb = j * fa::kFwdBC;
+      const bool ragged = kb + fa::kFwdBC > N;
+      const bool diag = causal && (kb + fa::kFwdBC - 1 > qt * fa::kFwdBR);
+      if (ragged || diag) ++masked;
+    }
+  }
+  out->tiles_visited = visited * B * H;
+  out->tiles_masked = masked * B * H;
+  return ok();
+}
+
+int fa_decode_chunk_tokens(int kv_len, int num_splits) {
+  return fa::decode_chunk_tokens(kv_len, num_splits);
+}
+
+int fa_decode_plan(int B, int H, int d, int num_splits, fa_decode_plan_t* out) {
+  if (!out) return fail(FA_ERR_INVALID_ARG, "null plan pointer");
+  if (B < 1 || H < 1) return fail(FA_ERR_INVALID_ARG, "B, H must be >= 1");
+  if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "head dimension %d not supported", d);
+  if (num_splits < 0 || num_splits > 4096) return fail(FA_ERR_INVALID_ARG, "num_splits out of range");
+  int S = num_splits;
+  if (S == 0) S = auto_splits(B, H, 256);
+  out->num_splits = S;
+  out->threads_per_workgroup = fa::kDecWaves * 64;
+  out->split_workgroups = (int64_t)B * H * S;
+  out->combine_workgroups = (int64_t)B * H;
+  out->workspace_bytes = ws_bytes(B, H, d, S);
+  return ok();
+}
+
+size_t fa_decode_workspace_bytes(int B, int H, int d, int num_splits) {
+  if (B < 1 || H < 1 || (d != 64 && d != 128) || num_splits < 0 || num_splits > 4096) return 0;
+  int S = num_splits;
+  if (S == 0) {
+    int cus = 0;
+    if (cu_count(&cus) != FA_OK) return 0;
+    S = auto_splits(B, H, cus);
+  }
+  return ws_bytes(B, H, d, S);
+}
+
+int fa_decode(const void* q, const void* Kcache, const void* Vcache, void* o, int B, int H,
+              const int32_t* Lkv, int d, int num_splits, void* stream) {
+  const float scale = 1.f / sqrtf((float)d);
+  int st = check_decode(q, Kcache, Vcache, o, nullptr, B, H, Lkv, 0, d, num_splits, scale);
+  if (st != FA_OK) return st;
+  int S = num_splits;
+  if (S == 0) {
+    int cus = 0;
+    if ((st = cu_count(&cus)) != FA_OK) return st;
+    S = auto_splits(B, H, cus);
+  }
+  const size_t need = ws_bytes(B, H, d, S);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  void* ws = nullptr;
+  {
+    std::lock_guard<std::mutex> lk(g_ws_mu);
+    Workspace& w = g_ws[std::make_pair(dev, hs)];
+    if (w.bytes < need) {
+      hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+      e = hipStreamIsCapturing(hs, &cs);
+      if (e != hipSuccess) return hip_fail(e, "hipStreamIsCapturing");
+      if (cs != hipStreamCaptureStatusNone)
+        return fail(FA_ERR_WORKSPACE, "fa_decode workspace must grow to %zu bytes; call once outside stream capture", need);
+      if (w.ptr) {
+        e = hipStreamSynchronize(hs);
+        if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+        e = hipFree(w.ptr);
+        w.ptr = nullptr;
+        w.bytes = 0;
+        if (e != hipSuccess) return hip_fail(e, "hipFree");
+      }
+      e = hipMalloc(&w.ptr, need);
+      if (e != hipSuccess) {
+        w.ptr = nullptr;
+        (void)hipGetLastError();
+        return fail(FA_ERR_NOMEM, "hipMalloc(%zu) for the decode workspace failed", need);
+      }
+      w.bytes = need;
+    }
+    ws = w.ptr;
+  }
+  return decode_common(q, Kcache, Vcache, o, nullptr, B, H, Lkv, 0, d, S, scale, ws, hs);
+}
+
+int fa_decode_ex(const void* q, const void* Kcache, const void* Vcache, void* o, float* lse_out,
+                 int B, int H, const int32_t* Lkv, int kv_seq_capacity, int d, int num_splits,
+                 float scale, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_decode(q, Kcache, Vcache, o, lse_out, B, H, Lkv, kv_seq_capacity, d, num_splits, scale);
+  if (st != FA_OK) return st;
+  if (!workspace) return fail(FA_ERR_WORKSPACE, "null workspace");
+  if (!aligned(workspace, 256)) return fail(FA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  int S = num_splits;
+  if (S == 0) {
+    int cus = 0;
+    if ((st = cu_count(&cus)) != FA_OK) return st;
+    S = auto_splits(B, H, cus);
+  }
+  const size_t need = ws_bytes(B, H, d, S);
+  if (workspace_bytes < need)
+    return fail(FA_ERR_WORKSPACE, "workspace of %zu bytes is too small (%zu needed)", workspace_bytes, need);
+  if (overlap(workspace, need, o, (size_t)B * H * d * 2) || overlap(workspace, need, q, (size_t)B * H * d * 2))
+    return fail(FA_ERR_INVALID_ARG, "workspace overlaps q or o");
+  return decode_common(q, Kcache, Vcache, o, lse_out, B, H, Lkv, kv_seq_capacity, d, S, scale,
+                       workspace, static_cast<hipStream_t>(stream));
+}
+
+int fa_release_workspace(void) {
+  std::lock_guard<std::mutex> lk(g_ws_mu);
+  int prev = 0;
+  hipError_t e = hipGetDevice(&prev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  int status = FA_OK;
+  for (auto& kv : g_ws) {
+    if (!kv.second.ptr) continue;
+    if ((e = hipSetDevice(kv.first.first)) == hipSuccess && (e = hipDeviceSynchronize()) == hipSuccess)
+      e = hipFree(kv.second.ptr);
+    if (e != hipSuccess) status = hip_fail(e, "releasing a decode workspace");
+    kv.second.ptr = nullptr;
+    kv.second.bytes = 0;
+  }
+  g_ws.clear();
+  (void)hipSetDevice(prev);
+  return status;
+}
+
+}  // extern "C"

@@ -1,0 +1,78 @@
+// Internal declarations shared by the host dispatch (fa_api.hip) and the
+// kernel translation units.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+// Prefill tiling, shared by the planner and the bf16 kernel: a workgroup of
+// kFwdWaves wavefronts owns kFwdBR query rows (32 per wavefront) and walks
+// KV tiles of kFwdBC keys.
+constexpr int kFwdWaves = 4;
+constexpr int kFwdBR = 32 * kFwdWaves;
+constexpr int kFwdBC = 64;
+
+// fp32 prefill: one wavefront, one query row per lane, 64-key tiles.
+constexpr int kF32BR = 64;
+constexpr int kF32BC = 64;
+
+// Decode split kernel: wavefronts per workgroup; chunk lengths are rounded up
+// to a multiple of kDecChunkAlign tokens.
+constexpr int kDecWaves = 4;
+constexpr int kDecChunkAlign = 64;
+
+struct FwdArgs {
+  const void* Q;
+  const void* K;
+  const void* V;
+  void* O;
+  float* L;
+  int B, H, N;
+  int causal;
+  float scale;
+};
+
+struct DecodeArgs {
+  const void* q;
+  const void* K;
+  const void* V;
+  void* o;
+  float* lse_out;
+  const int32_t* Lkv;
+  float* part_o;    // [B, H, S, d]
+  float* part_lse;  // [B, H, S]
+  int B, H, S;
+  int capacity;     // 0 = packed
+  float scale;
+};
+
+// Launchers: enqueue on `stream`, return hipGetLastError().
+hipError_t launch_fwd_bf16(const FwdArgs& a, int d, hipStream_t stream);
+hipError_t launch_fwd_f32(const FwdArgs& a, int d, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs& a, int d, hipStream_t stream);
+
+// Host-side tile bookkeeping used by both the planner and the launcher.
+__host__ __device__ inline int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Number of KV tiles that query tile `qt` visits (causal tiles wholly in the
+// future are skipped).
+inline int fwd_kv_tiles_for(int qt, int N, int causal) {
+  int kv_tiles = (int)ceil_div64(N, kFwdBC);
+  if (!causal) return kv_tiles;
+  int last_row = (qt + 1) * kFwdBR - 1;
+  if (last_row > N - 1) last_row = N - 1;
+  int t = last_row / kFwdBC + 1;
+  return t < kv_tiles ? t : kv_tiles;
+}
+
+// Decode chunk length for a sequence of `len` tokens split `S` ways.
+__host__ __device__ inline int decode_chunk_tokens(int len, int S) {
+  if (len <= 0 || S <= 0) return 0;
+  int64_t c = ceil_div64(len, S);
+  c = ceil_div64(c, kDecChunkAlign) * kDecChunkAlign;
+  return (int)c;
+}
+
+}  // namespace fa

@@ -1,0 +1,172 @@
+/*
+ * fa.h -- exact attention forward (FlashAttention) and single-query
+ * Flash-Decoding for AMD MI355X (gfx950).  C ABI.
+ *
+ * Sources, cited by page title and section:
+ *  [FA]  "Infra: Flash Attention" (pufanyi.com blog): "Attention and scope"
+ *        (S = Q K^T / sqrt(d), row softmax, O = P V), "Tiled computation and
+ *        forward" (Algorithm 1, FlashAttention forward; boundary conditions),
+ *        "Backward and recomputation" (L_i = m_i + log l_i), "Prefill and
+ *        decode".
+ *  [FD]  airsota interview card "Efficient attention & FlashAttention"
+ *        (science-depth M4-055), section 3 "Mathematical principles &
+ *        derivation": Flash-Decoding steps 1-3 (split the KV sequence into
+ *        chunks, one partial (O^(k), m^(k), l^(k)) per chunk, log-sum-exp
+ *        reduction), section 4 (choice of the chunk count).
+ *  [L18] "CMU 10-423 Lecture 18" notes: section 3.4 (FA-2 loop order),
+ *        section 4.3 (causal masks skip whole tiles).
+ *
+ * Conventions shared by every entry point
+ *  - Tensors are dense, row-major, with the head dimension d contiguous.
+ *    Prefill tensors are [B, H, N, d]; L is [B, H, N].
+ *  - Pointers documented as "device" must be device (or managed) memory on the
+ *    current HIP device, 16-byte aligned.  The caller owns every buffer; the
+ *    library neither frees nor retains caller pointers.  Outputs are fully
+ *    overwritten and must not overlap any input.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
+ *    work is enqueued asynchronously on it; nothing here synchronises.
+ *  - Return value: FA_OK (0) or a negative fa_status.  Arguments are validated
+ *    on the host before any HIP call; an invalid call enqueues nothing.
+ *    fa_last_error() then holds a message (thread-local).  Faults inside a
+ *    kernel surface at the caller's next synchronisation, as for any HIP work.
+ *  - Supported head dimensions: d = 64 and d = 128.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fa_status {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARG = -1, /* null/misaligned pointer, bad size or flag */
+  FA_ERR_UNSUPPORTED = -2, /* valid request this build does not implement (e.g. d) */
+  FA_ERR_HIP = -3,         /* a HIP runtime call or kernel launch failed */
+  FA_ERR_NOMEM = -4,       /* the internal workspace could not be allocated */
+  FA_ERR_WORKSPACE = -5    /* caller workspace missing or too small */
+} fa_status;
+
+/* Geometry of one fa_fwd launch (host-only planning; see fa_fwd_plan). */
+typedef struct fa_fwd_plan_t {
+  int block_rows;            /* B_r: query rows per workgroup */
+  int block_cols;            /* B_c: keys per KV tile */
+  int q_tiles;               /* ceil(N / B_r) per (b, h) */
+  int kv_tiles;              /* ceil(N / B_c) per (b, h) */
+  int threads_per_workgroup; /* wavefronts * 64 */
+  int lds_bytes;             /* LDS per workgroup */
+  int64_t workgroups;        /* B * H * q_tiles */
+  int64_t tiles_visited;     /* (query tile, KV tile) pairs computed, all heads */
+  int64_t tiles_masked;      /* of those, tiles masked on chip (diagonal/ragged) */
+} fa_fwd_plan_t;
+
+/* Geometry of one fa_decode launch (host-only planning; see fa_decode_plan). */
+typedef struct fa_decode_plan_t {
+  int num_splits;            /* chunks per (b, h) actually used */
+  int threads_per_workgroup; /* split kernel */
+  int64_t split_workgroups;  /* B * H * num_splits */
+  int64_t combine_workgroups;/* B * H */
+  size_t workspace_bytes;    /* partials: B*H*num_splits*(d + 1) floats, aligned */
+} fa_decode_plan_t;
+
+/*
+ * fa_fwd -- FlashAttention forward, bf16 inputs ([FA] Algorithm 1, FA-2 order
+ * per [L18] section 3.4).
+ *   Q, K, V : device bf16 [B, H, N, d]
+ *   O       : device bf16 [B, H, N, d], O = softmax(Q K^T * scale) V, each
+ *             element rounded to nearest-even from fp32
+ *   L       : device fp32 [B, H, N], natural-log log-sum-exp of the scaled
+ *             scores of each row, L_i = m_i + log l_i; may be NULL (not written)
+ *   causal  : 0 or 1; 1 keeps key j for query i iff j <= i (square, top-left
+ *             aligned).  Tiles wholly above the diagonal are not visited
+ *             ([L18] section 4.3).
+ *   scale   : finite, > 0 (1/sqrt(d) for the pages' definition)
+ * Arithmetic: bf16 MFMA products with fp32 accumulation; the softmax state
+ * (m, l, U) is fp32; the probabilities fed to the second product are rounded
+ * to bf16.  Errors: FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED (d), FA_ERR_HIP.
+ */
+int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* L, int B, int H,
+           int N, int d, int causal, float scale, void* stream);
+
+/*
+ * fa_fwd_f32 -- the same contract with fp32 Q, K, V, O (device fp32
+ * [B, H, N, d]); every operation is fp32 (no reduced-precision step).
+ */
+int fa_fwd_f32(const float* Q, const float* K, const float* V, float* O, float* L, int B,
+               int H, int N, int d, int causal, float scale, void* stream);
+
+/*
+ * fa_decode -- Flash-Decoding of one query per (b, h) against a KV cache
+ * ([FA] "Prefill and decode"; [FD] section 3 steps 1-3).
+ *   q       : device bf16 [B, H, d] (the newest token's query)
+ *   Kcache, Vcache : device bf16, packed by sequence: sequence b occupies a
+ *             [H, Lkv[b], d] block and the blocks follow each other in b
+ *             order (so equal lengths give plain [B, H, L, d])
+ *   o       : device bf16 [B, H, d]
+ *   Lkv     : device int32 [B], per-sequence cache lengths (>= 0).  A length
+ *             of 0 gives o = 0 for that sequence.
+ *   num_splits : chunks per (b, h); 0 = automatic (from the device's compute
+ *             unit count and B * H).  Sequence b is cut into chunks of
+ *             ceil(Lkv[b] / num_splits) tokens rounded up to a multiple of 64;
+ *             trailing chunks may be empty.
+ * The query attends to every cached key with scale 1/sqrt(d).  Partials go to
+ * an internal workspace owned by the library, one per (device, stream), grown
+ * on demand with hipMalloc (so not while the stream is being captured) and
+ * released by fa_release_workspace().  Errors: FA_ERR_INVALID_ARG,
+ * FA_ERR_UNSUPPORTED, FA_ERR_NOMEM, FA_ERR_HIP.
+ */
+int fa_decode(const void* q, const void* Kcache, const void* Vcache, void* o, int B, int H,
+              const int32_t* Lkv, int d, int num_splits, void* stream);
+
+/*
+ * fa_decode_ex -- fa_decode with every option explicit.
+ *   lse_out         : device fp32 [B, H] or NULL; natural-log log-sum-exp of
+ *                     the query's scaled scores (-inf for an empty cache)
+ *   kv_seq_capacity : 0 = packed layout as in fa_decode; > 0 = padded layout
+ *                     [B, H, kv_seq_capacity, d] with Lkv[b] <= capacity
+ *                     (lengths above it are clamped to it)
+ *   scale           : finite, > 0
+ *   workspace       : caller-owned device memory of at least
+ *                     fa_decode_workspace_bytes(B, H, d, num_splits) bytes,
+ *                     256-byte aligned; it must not be shared by calls that
+ *                     may run concurrently.
+ * Allocates nothing.  Errors: as fa_decode, plus FA_ERR_WORKSPACE.
+ */
+int fa_decode_ex(const void* q, const void* Kcache, const void* Vcache, void* o,
+                 float* lse_out, int B, int H, const int32_t* Lkv, int kv_seq_capacity, int d,
+                 int num_splits, float scale, void* workspace, size_t workspace_bytes,
+                 void* stream);
+
+/* Workspace bytes fa_decode_ex needs; num_splits = 0 resolves the automatic
+ * count on the current device.  Returns 0 for invalid arguments. */
+size_t fa_decode_workspace_bytes(int B, int H, int d, int num_splits);
+
+/* Host-only launch planning (no HIP call; usable without a GPU).
+ * fa_fwd_plan: tile geometry and the exact number of tiles fa_fwd visits.
+ * fa_decode_plan: splits and workspace; num_splits = 0 needs the device's CU
+ * count, so without a device it assumes 256 compute units.
+ * fa_decode_chunk_tokens: chunk length for a sequence of kv_len tokens. */
+int fa_fwd_plan(int B, int H, int N, int d, int causal, fa_fwd_plan_t* out);
+int fa_decode_plan(int B, int H, int d, int num_splits, fa_decode_plan_t* out);
+int fa_decode_chunk_tokens(int kv_len, int num_splits);
+
+/* Frees fa_decode's internal workspaces (synchronises the devices that own
+ * them).  Returns FA_OK or FA_ERR_HIP. */
+int fa_release_workspace(void);
+
+/* Static description of a status code, and the thread-local message of the
+ * last failing call on this thread ("" if none). */
+const char* fa_status_string(int status);
+const char* fa_last_error(void);
+
+/* Library ABI version: (major << 16) | minor. */
+int fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

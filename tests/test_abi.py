@@ -1,0 +1,178 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, rejects invalid arguments before any HIP call, and plans
+launches whose geometry matches the oracle's tile accounting."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _fa():
+    import exact_io_aware_02_amd as fa
+
+    return fa
+
+
+def _header_functions():
+    text = open(os.path.join(ROOT, "include", "fa.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w]+\*?\s+\**(fa_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_symbols_exported():
+    fa = _fa()
+    names = _header_functions()
+    assert len(names) >= 12, names
+    assert sorted(fa.EXPORTED) == names
+    for n in names:
+        assert hasattr(fa.lib, n), n
+
+
+def test_status_strings():
+    fa = _fa()
+    assert fa.status_string(0) == "ok"
+    for s in (-1, -2, -3, -4, -5):
+        assert fa.status_string(s) not in ("", "unknown status")
+    assert fa.status_string(7) == "unknown status"
+
+
+A = 1 << 20  # a 16-byte-aligned fake address; only used where validation rejects first
+
+
+def _fwd(fn, Q=A, K=2 * A, V=3 * A, O=4 * A, L=None, B=1, H=1, N=16, d=64, causal=0, scale=0.125):
+    lib = _fa().lib
+    return getattr(lib, fn)(Q, K, V, O, L, B, H, N, d, causal, ctypes.c_float(scale), None)
+
+
+@pytest.mark.parametrize("fn", ["fa_fwd", "fa_fwd_f32"])
+@pytest.mark.parametrize(
+    "kw,status,msg",
+    [
+        (dict(Q=None), -1, "null"),
+        (dict(O=None), -1, "null"),
+        (dict(B=0), -1, ">= 1"),
+        (dict(H=-1), -1, ">= 1"),
+        (dict(N=0), -1, ">= 1"),
+        (dict(d=0), -1, "d must"),
+        (dict(d=96), -2, "not supported"),
+        (dict(d=256), -2, "not supported"),
+        (dict(causal=2), -1, "causal"),
+        (dict(scale=0.0), -1, "scale"),
+        (dict(scale=-1.0), -1, "scale"),
+        (dict(scale=float("inf")), -1, "scale"),
+        (dict(scale=float("nan")), -1, "scale"),
+        (dict(Q=A + 4), -1, "aligned"),
+        (dict(O=A), -1, "overlaps"),
+        (dict(O=2 * A + 64), -1, "overlaps"),
+        (dict(L=4 * A + 8), -1, "overlaps"),
+        (dict(L=5 * A + 2), -1, "aligned"),
+    ],
+)
+def test_fwd_rejects_invalid_arguments(fn, kw, status, msg):
+    fa = _fa()
+    assert _fwd(fn, **kw) == status
+    assert msg in fa.last_error()
+
+
+def _dec(q=A, Kc=2 * A, Vc=3 * A, o=4 * A, B=1, H=1, Lkv=5 * A, d=64, splits=0):
+    return _fa().lib.fa_decode(q, Kc, Vc, o, B, H, Lkv, d, splits, None)
+
+
+@pytest.mark.parametrize(
+    "kw,status,msg",
+    [
+        (dict(q=None), -1, "null"),
+        (dict(Lkv=None), -1, "null"),
+        (dict(B=0), -1, ">= 1"),
+        (dict(H=70000), -1, "65535"),
+        (dict(d=100), -2, "not supported"),
+        (dict(splits=-1), -1, "num_splits"),
+        (dict(splits=5000), -1, "num_splits"),
+        (dict(Kc=2 * A + 8), -1, "aligned"),
+        (dict(Lkv=5 * A + 2), -1, "misaligned"),
+        (dict(o=A), -1, "overlaps"),
+    ],
+)
+def test_decode_rejects_invalid_arguments(kw, status, msg):
+    fa = _fa()
+    assert _dec(**kw) == status
+    assert msg in fa.last_error()
+
+
+def test_decode_ex_rejects_bad_workspace_and_capacity():
+    fa = _fa()
+    lib = fa.lib
+    args = (A, 2 * A, 3 * A, 4 * A, None, 2, 4, 5 * A)
+    # negative capacity
+    assert lib.fa_decode_ex(*args, -1, 128, 8, ctypes.c_float(0.1), 6 * A, 1 << 20, None) == -1
+    # bad scale
+    assert lib.fa_decode_ex(*args, 0, 128, 8, ctypes.c_float(0.0), 6 * A, 1 << 20, None) == -1
+    # missing workspace
+    assert lib.fa_decode_ex(*args, 0, 128, 8, ctypes.c_float(0.1), None, 1 << 20, None) == -5
+    # misaligned workspace
+    assert lib.fa_decode_ex(*args, 0, 128, 8, ctypes.c_float(0.1), 6 * A + 16, 1 << 20, None) == -5
+    # too small (explicit split count: no device query needed)
+    need = 2 * 4 * 8 * 128 * 4 + 256
+    assert lib.fa_decode_ex(*args, 0, 128, 8, ctypes.c_float(0.1), 6 * A, need - 1, None) == -5
+    assert "too small" in fa.last_error()
+
+
+def test_decode_workspace_formula():
+    fa = _fa()
+    for B, H, d, S in [(1, 32, 128, 64), (8, 32, 128, 8), (3, 5, 64, 7)]:
+        parts = B * H * S
+        a256 = lambda x: (x + 255) // 256 * 256
+        assert fa.fa_decode_workspace_bytes(B, H, d, S) == a256(parts * d * 4) + a256(parts * 4)
+        p = fa.fa_decode_plan(B, H, d, S)
+        assert p["num_splits"] == S and p["split_workgroups"] == B * H * S
+        assert p["workspace_bytes"] == fa.fa_decode_workspace_bytes(B, H, d, S)
+    assert fa.fa_decode_workspace_bytes(0, 1, 128, 1) == 0
+    # automatic split count, planned for a 256-CU device: about 8 workgroups per CU
+    assert fa.fa_decode_plan(1, 32, 128, 0)["num_splits"] == 64
+    assert fa.fa_decode_plan(8, 32, 128, 0)["num_splits"] == 8
+
+
+@pytest.mark.parametrize("L", [1, 63, 64, 65, 511, 512, 4096, 32768, 65536, 40001])
+@pytest.mark.parametrize("S", [1, 2, 3, 7, 64, 256])
+def test_decode_chunks_cover_every_key_once(L, S):
+    fa = _fa()
+    c = fa.fa_decode_chunk_tokens(L, S)
+    assert c % 64 == 0 and c >= 64
+    covered = np.zeros(L, dtype=np.int64)
+    for s in range(S):
+        a, b = s * c, min(L, (s + 1) * c)
+        if a < b:
+            covered[a:b] += 1
+    assert np.all(covered == 1)
+    assert fa.fa_decode_chunk_tokens(0, S) == 0
+
+
+@pytest.mark.parametrize("causal", [0, 1])
+@pytest.mark.parametrize("N", [1, 64, 100, 128, 129, 1000, 2048])
+def test_fwd_plan_tile_count_matches_oracle(N, causal):
+    """The tiles fa_fwd visits are those of Algorithm 1 with B_r = 128,
+    B_c = 64 and whole-tile causal skipping, as counted by the oracle."""
+    fa = _fa()
+    p = fa.fa_fwd_plan(2, 3, N, 128, causal)
+    rng = np.random.default_rng(0)
+    Q, K, V = (rng.standard_normal((N, 2)) for _ in range(3))
+    _, _, cnt = oracle.tiled_ref(Q, K, V, p["block_rows"], p["block_cols"], 1.0, causal=bool(causal), count=True)
+    assert p["tiles_visited"] == 6 * cnt["tiles"]
+    assert p["workgroups"] == 6 * -(-N // 128)
+
+
+def test_fwd_plan_causal_pin_exercise4():
+    """With square tiles the causal count is T(T+1)/2 ('CMU 10-423 Lecture
+    18', Exercise 4); with B_r = 2 B_c each query tile covers two KV tiles,
+    so the count at N = 4096 is 2 * 32*33/2 per head."""
+    fa = _fa()
+    p = fa.fa_fwd_plan(1, 1, 4096, 128, 1)
+    assert p["tiles_visited"] == 2 * oracle.causal_tile_count(32)
+    assert fa.fa_fwd_plan(1, 1, 4096, 128, 0)["tiles_visited"] == 32 * 64

@@ -1,0 +1,347 @@
+"""Parity of the HIP path (through the C ABI) with the float64 oracle.
+
+Bars: bf16 inputs -- max|dO| <= 2e-2 and max|dL| <= 2e-3; fp32 inputs --
+max|dO| <= 1e-5 and max|dL| <= 1e-5 (absolute, max over the elements
+compared).  Small shapes are compared element by element; the full-size
+workloads are run in the same launch configuration the bench times and
+compared on sampled rows that the oracle computes one by one (every row of a
+decode workload is one such sample).
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+BF16_O, BF16_L = 2e-2, 2e-3
+F32_O, F32_L = 1e-5, 1e-5
+
+
+def _fa():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import exact_io_aware_02_amd as fa
+
+    return fa
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+
+
+def _host(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def _prefill_compare(Q, K, V, O, L, scale, causal, rows=None, heads=None):
+    """Compare device outputs with the oracle on the given (b, h) heads and
+    query rows (all when None).  Returns (max|dO|, max|dL|)."""
+    B, H, N, d = Q.shape
+    heads = heads if heads is not None else [(b, h) for b in range(B) for h in range(H)]
+    dO = dL = 0.0
+    for b, h in heads:
+        r = np.arange(N) if rows is None else np.asarray(rows)
+        q = _host(Q[b, h, torch.as_tensor(r, device=Q.device)])
+        k, v = _host(K[b, h]), _host(V[b, h])
+        o_ref, l_ref = oracle.attention_rows(q, k, v, scale, causal=causal, q_pos=r)
+        o_dev = _host(O[b, h, torch.as_tensor(r, device=O.device)])
+        l_dev = _host(L[b, h, torch.as_tensor(r, device=L.device)])
+        dO = max(dO, float(np.max(np.abs(o_dev - o_ref))))
+        dL = max(dL, float(np.max(np.abs(l_dev - l_ref))))
+    return dO, dL
+
+
+# --------------------------------------------------------------------------
+# fp32 path
+# --------------------------------------------------------------------------
+
+def test_fp32_small_workload_all_elements():
+    fa = _fa()
+    cfg = synth.WORKLOADS["fp32_small"]
+    _say("fp32_small", cfg)
+    Q, K, V = synth.prefill_inputs("fp32_small", "cuda")
+    O = torch.empty_like(Q)
+    L = torch.empty(Q.shape[:3], device="cuda", dtype=torch.float32)
+    scale = 1.0 / math.sqrt(cfg["d"])
+    fa.fa_fwd_f32(Q, K, V, O, L, causal=False, scale=scale)
+    torch.cuda.synchronize()
+    dO, dL = _prefill_compare(Q, K, V, O, L, scale, False)
+    print(f"fp32_small max|dO|={dO:.3e} max|dL|={dL:.3e}")
+    assert dO <= F32_O and dL <= F32_L
+
+
+def test_fp32_worked_example_49_over_15():
+    """'Infra: Flash Attention', worked example of the state merge: scores
+    log 1, log 2, log 4, log 8 against values 1, 2, 3, 4 give 49/15 and
+    L = log 15."""
+    fa = _fa()
+    _say("fp32 49/15 example")
+    d, N = 64, 4
+    Q = torch.zeros(1, 1, N, d, device="cuda")
+    K = torch.zeros_like(Q)
+    V = torch.zeros_like(Q)
+    Q[0, 0, :, 0] = 1.0
+    K[0, 0, :, 0] = torch.tensor([math.log(1), math.log(2), math.log(4), math.log(8)])
+    V[0, 0, :, 0] = torch.tensor([1.0, 2.0, 3.0, 4.0])
+    O = torch.empty_like(Q)
+    L = torch.empty(1, 1, N, device="cuda")
+    fa.fa_fwd_f32(Q, K, V, O, L, causal=False, scale=1.0)
+    torch.cuda.synchronize()
+    assert abs(O[0, 0, 0, 0].item() - 49 / 15) <= 1e-6
+    assert abs(L[0, 0, 0].item() - math.log(15)) <= 1e-6
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [1, 63, 65, 200])
+def test_fp32_small_shapes(N, d, causal):
+    fa = _fa()
+    _say("fp32", N, d, causal)
+    shape = (2, 3, N, d)
+    Q, K, V = (synth.torch_normal(100 + t, shape, "cuda", "f32") for t in range(3))
+    O = torch.empty_like(Q)
+    L = torch.empty(shape[:3], device="cuda")
+    fa.fa_fwd_f32(Q, K, V, O, L, causal=causal)
+    torch.cuda.synchronize()
+    dO, dL = _prefill_compare(Q, K, V, O, L, 1 / math.sqrt(d), causal)
+    assert dO <= F32_O and dL <= F32_L, (dO, dL)
+
+
+# --------------------------------------------------------------------------
+# bf16 prefill
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [1, 17, 64, 127, 128, 129, 300, 1000])
+def test_bf16_small_shapes(N, d, causal):
+    fa = _fa()
+    _say("bf16", N, d, causal)
+    shape = (2, 2, N, d)
+    Q, K, V = (synth.torch_normal(200 + t, shape, "cuda", "bf16") for t in range(3))
+    O = torch.empty_like(Q)
+    L = torch.empty(shape[:3], device="cuda")
+    fa.fa_fwd(Q, K, V, O, L, causal=causal)
+    torch.cuda.synchronize()
+    dO, dL = _prefill_compare(Q, K, V, O, L, 1 / math.sqrt(d), causal)
+    assert dO <= BF16_O and dL <= BF16_L, (dO, dL)
+
+
+def test_bf16_large_values_and_scale():
+    """Scores with a wide spread (values x4, scale 0.5) exercise the running
+    maximum and the alpha rescale across many tiles."""
+    fa = _fa()
+    _say("bf16 wide scores")
+    shape = (1, 2, 777, 128)
+    Q, K, V = (synth.torch_normal(300 + t, shape, "cuda", "bf16", vscale=4.0) for t in range(3))
+    O = torch.empty_like(Q)
+    L = torch.empty(shape[:3], device="cuda")
+    for causal in (False, True):
+        fa.fa_fwd(Q, K, V, O, L, causal=causal, scale=0.05)
+        torch.cuda.synchronize()
+        dO, dL = _prefill_compare(Q, K, V, O, L, 0.05, causal)
+        assert dO <= 4 * BF16_O and dL <= BF16_L, (causal, dO, dL)
+
+
+def test_bf16_L_optional_and_deterministic():
+    fa = _fa()
+    _say("bf16 determinism")
+    shape = (1, 4, 1000, 128)
+    Q, K, V = (synth.torch_normal(400 + t, shape, "cuda", "bf16") for t in range(3))
+    O1, O2 = torch.empty_like(Q), torch.empty_like(Q)
+    L1 = torch.empty(shape[:3], device="cuda")
+    fa.fa_fwd(Q, K, V, O1, L1, causal=True)
+    fa.fa_fwd(Q, K, V, O2, None, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(O1, O2)
+
+
+def _rows_sample(N, seed):
+    rng = np.random.default_rng(seed)
+    fixed = [0, 1, 31, 32, 63, 64, 127, 128, 129, N // 2, N - 129, N - 128, N - 65, N - 64, N - 2, N - 1]
+    return np.unique(np.concatenate([fixed, rng.integers(0, N, 32)]))
+
+
+def test_bf16_prefill_8k_workload_sampled():
+    fa = _fa()
+    cfg = synth.WORKLOADS["prefill_8k"]
+    _say("prefill_8k", cfg)
+    Q, K, V = synth.prefill_inputs("prefill_8k", "cuda")
+    O = torch.empty_like(Q)
+    L = torch.empty(Q.shape[:3], device="cuda")
+    fa.fa_fwd(Q, K, V, O, L, causal=False)
+    torch.cuda.synchronize()
+    rows = _rows_sample(cfg["N"], 1)
+    dO, dL = _prefill_compare(Q, K, V, O, L, 1 / math.sqrt(cfg["d"]), False, rows=rows,
+                              heads=[(0, 0), (0, 7), (0, 18), (0, 31)])
+    print(f"prefill_8k sampled max|dO|={dO:.3e} max|dL|={dL:.3e}")
+    assert dO <= BF16_O and dL <= BF16_L
+    assert torch.isfinite(O).all() and torch.isfinite(L).all()
+
+
+def test_bf16_causal_4k_workload_sampled():
+    fa = _fa()
+    cfg = synth.WORKLOADS["causal_4k"]
+    _say("causal_4k", cfg)
+    Q, K, V = synth.prefill_inputs("causal_4k", "cuda")
+    O = torch.empty_like(Q)
+    L = torch.empty(Q.shape[:3], device="cuda")
+    fa.fa_fwd(Q, K, V, O, L, causal=True)
+    torch.cuda.synchronize()
+    rows = _rows_sample(cfg["N"], 2)
+    dO, dL = _prefill_compare(Q, K, V, O, L, 1 / math.sqrt(cfg["d"]), True, rows=rows,
+                              heads=[(0, 0), (1, 5), (2, 17), (3, 31)])
+    print(f"causal_4k sampled max|dO|={dO:.3e} max|dL|={dL:.3e}")
+    assert dO <= BF16_O and dL <= BF16_L
+    # causal row 0 sees only key 0: O_0 = V_0 exactly up to output rounding
+    assert torch.equal(O[:, :, 0], V[:, :, 0])
+    assert torch.isfinite(O).all() and torch.isfinite(L).all()
+
+
+# --------------------------------------------------------------------------
+# decode
+# --------------------------------------------------------------------------
+
+def _decode_oracle(q, Kc, Vc, lengths, H, d, b, h, scale, capacity=0):
+    if capacity:
+        base = (b * H + h) * capacity * d
+    else:
+        base = int(synth.packed_offsets(lengths, H, d)[b]) + h * int(lengths[b]) * d
+    Lb = int(lengths[b])
+    k = _host(Kc.view(-1)[base:base + Lb * d]).reshape(Lb, d)
+    v = _host(Vc.view(-1)[base:base + Lb * d]).reshape(Lb, d)
+    return oracle.decode_ref(_host(q[b, h]), k, v, scale)
+
+
+def _decode_compare(q, Kc, Vc, o, lengths, lse=None, pairs=None, scale=None, capacity=0):
+    B, H, d = q.shape
+    scale = scale or 1 / math.sqrt(d)
+    pairs = pairs if pairs is not None else [(b, h) for b in range(B) for h in range(H)]
+    dO = dL = 0.0
+    for b, h in pairs:
+        o_ref, l_ref = _decode_oracle(q, Kc, Vc, lengths, H, d, b, h, scale, capacity)
+        dO = max(dO, float(np.max(np.abs(_host(o[b, h]) - o_ref))))
+        if lse is not None:
+            ld = float(lse[b, h].item())
+            if l_ref == -np.inf:
+                assert ld == -np.inf
+            else:
+                dL = max(dL, abs(ld - l_ref))
+    return dO, dL
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("splits", [1, 3, 7, 64, 0])
+def test_decode_small(d, splits):
+    fa = _fa()
+    _say("decode small", d, splits)
+    lengths = np.array([1, 63, 1000, 0, 200], dtype=np.int64)
+    B, H = len(lengths), 3
+    total = int(lengths.sum()) * H * d
+    q = synth.torch_normal(500, (B, H, d), "cuda")
+    Kc = synth.torch_normal(501, (total,), "cuda")
+    Vc = synth.torch_normal(502, (total,), "cuda")
+    Lkv = torch.tensor(lengths, dtype=torch.int32, device="cuda")
+    o = torch.empty_like(q)
+    fa.fa_decode(q, Kc, Vc, o, Lkv, num_splits=splits)
+    ws = torch.empty(fa.fa_decode_workspace_bytes(B, H, d, splits), dtype=torch.uint8, device="cuda")
+    o2 = torch.empty_like(q)
+    lse = torch.empty(B, H, device="cuda")
+    fa.fa_decode_ex(q, Kc, Vc, o2, Lkv, ws, lse_out=lse, num_splits=splits)
+    torch.cuda.synchronize()
+    dO, _ = _decode_compare(q, Kc, Vc, o, lengths)
+    dO2, dL2 = _decode_compare(q, Kc, Vc, o2, lengths, lse=lse)
+    assert dO <= BF16_O and dO2 <= BF16_O and dL2 <= BF16_L, (dO, dO2, dL2)
+    assert torch.all(o[3] == 0)  # empty cache -> o = 0
+
+
+def test_decode_padded_layout_and_scale():
+    fa = _fa()
+    _say("decode padded")
+    B, H, d, cap = 3, 4, 128, 1500
+    lengths = np.array([1500, 7, 777], dtype=np.int64)
+    q = synth.torch_normal(510, (B, H, d), "cuda")
+    Kc = synth.torch_normal(511, (B, H, cap, d), "cuda")
+    Vc = synth.torch_normal(512, (B, H, cap, d), "cuda")
+    Lkv = torch.tensor(lengths, dtype=torch.int32, device="cuda")
+    o = torch.empty_like(q)
+    lse = torch.empty(B, H, device="cuda")
+    ws = torch.empty(fa.fa_decode_workspace_bytes(B, H, d, 5), dtype=torch.uint8, device="cuda")
+    fa.fa_decode_ex(q, Kc, Vc, o, Lkv, ws, lse_out=lse, kv_seq_capacity=cap, num_splits=5, scale=0.3)
+    torch.cuda.synchronize()
+    dO, dL = _decode_compare(q, Kc, Vc, o, lengths, lse=lse, scale=0.3, capacity=cap)
+    assert dO <= BF16_O and dL <= BF16_L, (dO, dL)
+
+
+def test_decode_split_invariance_and_prefill_row():
+    """The merge is order-free ('Infra: Flash Attention', Prefill and
+    decode): any split count gives the same answer within rounding; and the
+    decode of a query equals that query's row of non-causal prefill."""
+    fa = _fa()
+    _say("decode split invariance")
+    B, H, N, d = 1, 2, 2048, 128
+    Q, K, V = (synth.torch_normal(520 + t, (B, H, N, d), "cuda") for t in range(3))
+    O = torch.empty_like(Q)
+    L = torch.empty(B, H, N, device="cuda")
+    fa.fa_fwd(Q, K, V, O, L, causal=False)
+    Lkv = torch.full((B,), N, dtype=torch.int32, device="cuda")
+    q = Q[:, :, 100].contiguous()
+    outs = []
+    for s in (1, 2, 5, 32, 0):
+        o = torch.empty_like(q)
+        fa.fa_decode(q, K, V, o, Lkv, num_splits=s)
+        outs.append(o)
+    torch.cuda.synchronize()
+    for o in outs:
+        assert float((o.float() - outs[0].float()).abs().max()) <= 2 * BF16_O
+        assert float((o.float() - O[:, :, 100].float()).abs().max()) <= 2 * BF16_O
+    dO, _ = _decode_compare(q, K, V, outs[-1], np.array([N]))
+    assert dO <= BF16_O
+
+
+def test_decode_32k_workload_all_heads():
+    fa = _fa()
+    cfg = synth.WORKLOADS["decode_32k"]
+    _say("decode_32k", cfg)
+    q, Kc, Vc, lengths = synth.decode_inputs("decode_32k", "cuda")
+    Lkv = torch.tensor(lengths, dtype=torch.int32, device="cuda")
+    o = torch.empty_like(q)
+    fa.fa_decode(q, Kc, Vc, o, Lkv, num_splits=0)
+    B, H, d = q.shape
+    ws = torch.empty(fa.fa_decode_workspace_bytes(B, H, d, 64), dtype=torch.uint8, device="cuda")
+    o64 = torch.empty_like(q)
+    lse = torch.empty(B, H, device="cuda")
+    fa.fa_decode_ex(q, Kc, Vc, o64, Lkv, ws, lse_out=lse, num_splits=64)
+    torch.cuda.synchronize()
+    dO, _ = _decode_compare(q, Kc, Vc, o, lengths)
+    dO64, dL64 = _decode_compare(q, Kc, Vc, o64, lengths, lse=lse)
+    print(f"decode_32k max|dO|={dO:.3e} (auto) {dO64:.3e} (64 splits) max|dL|={dL64:.3e}")
+    assert dO <= BF16_O and dO64 <= BF16_O and dL64 <= BF16_L
+
+
+def test_decode_varlen_workload_sampled():
+    fa = _fa()
+    cfg = synth.WORKLOADS["decode_varlen"]
+    q, Kc, Vc, lengths = synth.decode_inputs("decode_varlen", "cuda")
+    _say("decode_varlen", cfg, "lengths", lengths.tolist())
+    Lkv = torch.tensor(lengths, dtype=torch.int32, device="cuda")
+    o = torch.empty_like(q)
+    fa.fa_decode(q, Kc, Vc, o, Lkv, num_splits=0)
+    B, H, d = q.shape
+    ws = torch.empty(fa.fa_decode_workspace_bytes(B, H, d, 0), dtype=torch.uint8, device="cuda")
+    lse = torch.empty(B, H, device="cuda")
+    o2 = torch.empty_like(q)
+    fa.fa_decode_ex(q, Kc, Vc, o2, Lkv, ws, lse_out=lse, num_splits=0)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2)
+    pairs = [(b, h) for b in range(B) for h in (0, 13, 31)]
+    dO, dL = _decode_compare(q, Kc, Vc, o2, lengths, lse=lse, pairs=pairs)
+    print(f"decode_varlen sampled max|dO|={dO:.3e} max|dL|={dL:.3e}")
+    assert dO <= BF16_O and dL <= BF16_L
+    assert torch.isfinite(o.float()).all()
