@@ -138,6 +138,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip causal_4k and decode_varlen")
     ap.add_argument("--num-splits", type=int, default=0, help="decode splits (0 = automatic)")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="before timing, run one plain device copy of this many MiB (calibrates "
+                         "HBM byte counters under rocprofv3)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -160,6 +163,16 @@ def main():
     torch.cuda.set_device(0)
     dev = "cuda"
     K_, W_ = args.steps, args.warmup
+
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log(f"copy probe: {args.copy_probe_mib} MiB read + {args.copy_probe_mib} MiB written")
 
     # ---------------- inputs (resident in HBM before timing)
     cfg = synth.WORKLOADS["prefill_8k"]

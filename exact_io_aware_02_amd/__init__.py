@@ -3,7 +3,7 @@ MI355X (gfx950).
 
 The compute lives in libfa.so (HIP kernels behind the C ABI of include/fa.h);
 this package is its ctypes binding.  Build the library in-tree with
-`python -m exact_io_aware_02_amd.build`.
+`python exact_io_aware_02_amd/build.py`.
 """
 
 from ._binding import (  # noqa: F401

@@ -55,7 +55,7 @@ class fa_decode_plan_t(ctypes.Structure):
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"{LIB_PATH} is missing: build it with `python -m exact_io_aware_02_amd.build` "
+            f"{LIB_PATH} is missing: build it with `python exact_io_aware_02_amd/build.py` "
             "(or __graft_entry__.build()); there is no non-HIP fallback"
         )
     lib = ctypes.CDLL(LIB_PATH)

@@ -1,6 +1,8 @@
 """Build libfa.so (the HIP kernels and the C ABI) in-tree for gfx950.
 
-    python -m exact_io_aware_02_amd.build [--verbose]
+    python exact_io_aware_02_amd/build.py [--verbose] [--resource-usage]
+
+(run as a script: importing the package would load the library first)
 
 Every source is compiled on each call (hipcc cross-compiles without a GPU).
 """
@@ -20,6 +22,10 @@ OBJDIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libfa.so")
 
 SOURCES = ["fa_api.hip", "fa_fwd_bf16.hip", "fa_fwd_f32.hip", "fa_decode.hip"]
+# NaN inputs are outside the contract of the bf16 kernels; without NaN
+# semantics fmaxf needs no canonicalisation and fuses into v_max3_f32.
+# Infinities stay honoured (masked scores are -inf).
+PER_SOURCE_FLAGS = {"fa_fwd_bf16.hip": ["-fno-honor-nans"], "fa_decode.hip": ["-fno-honor-nans"]}
 
 ARCH = "gfx950"
 # -packed-fp32-ops: keep the compiler from forming v_pk_{add,mul,fma}_f32
@@ -65,13 +71,27 @@ def build(verbose=False, resource_usage=False):
     for src in SOURCES:
         obj = os.path.join(OBJDIR, src.replace(".hip", ".o"))
         objs.append(obj)
-        cmds.append([hipcc, *FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj])
+        cmds.append([hipcc, *FLAGS, *PER_SOURCE_FLAGS.get(src, []), *extra, "-c",
+                     os.path.join(CSRC, src), "-o", obj])
     with ThreadPoolExecutor(max_workers=min(4, len(cmds))) as ex:
         list(ex.map(lambda c: _run(c, verbose or resource_usage), cmds))
     tmp = LIB + ".tmp"
     _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
+    _check_undefined(tmp)
     os.replace(tmp, LIB)
     return LIB
+
+
+def _check_undefined(path):
+    """Fail if the host pass dropped a kernel launch stub (the library would
+    then not load)."""
+    nm = shutil.which("nm") or shutil.which("llvm-nm")
+    if nm is None:
+        return
+    out = subprocess.run([nm, "-D", "--undefined-only", path], stdout=subprocess.PIPE, text=True).stdout
+    missing = [ln.split()[-1] for ln in out.splitlines() if "device_stub" in ln]
+    if missing:
+        raise RuntimeError("libfa.so references undefined kernel stubs: " + ", ".join(missing))
 
 
 if __name__ == "__main__":

@@ -56,7 +56,8 @@ int check_fwd(const void* Q, const void* K, const void* V, const void* O, const 
   if (L && !aligned(L, 4)) return fail(FA_ERR_INVALID_ARG, "L must be 4-byte aligned");
   const int64_t q_tiles = fa::ceil_div64(N, rows_per_wg);
   if ((int64_t)B * H * q_tiles > 0x7fffffffLL) return fail(FA_ERR_INVALID_ARG, "grid too large");
-  if ((int64_t)N > (1LL << 30)) return fail(FA_ERR_INVALID_ARG, "N too large");
+  if ((int64_t)N * d * (int64_t)elem > 0x7fffffffLL)
+    return fail(FA_ERR_INVALID_ARG, "one head of N x d elements must be under 2 GiB (N = %d)", N);
   const size_t tbytes = (size_t)B * H * N * d * elem;
   const size_t lbytes = L ? (size_t)B * H * N * sizeof(float) : 0;
   if (overlap(O, tbytes, Q, tbytes) || overlap(O, tbytes, K, tbytes) || overlap(O, tbytes, V, tbytes))
@@ -114,11 +115,14 @@ int cu_count(int* out) {
   return FA_OK;
 }
 
-// Automatic split count: enough workgroups for about eight per compute unit.
+// Automatic split count: enough split workgroups to cover every compute
+// unit once, and at least 8 chunks per sequence so that unequal lengths in a
+// batch still spread over the device.  Few long chunks stream better than
+// many short ones, and the combine stays small.
 int auto_splits(int B, int H, int cus) {
   const int64_t bh = (int64_t)B * H;
-  int64_t s = fa::ceil_div64(8LL * cus, bh);
-  if (s < 1) s = 1;
+  int64_t s = fa::ceil_div64(cus, bh);
+  if (s < 8) s = 8;
   if (s > 256) s = 256;
   return (int)s;
 }
@@ -203,7 +207,7 @@ int fa_fwd_plan(int B, int H, int N, int d, int causal, fa_fwd_plan_t* out) {
   out->q_tiles = q_tiles;
   out->kv_tiles = (int)fa::ceil_div64(N, fa::kFwdBC);
   out->threads_per_workgroup = fa::kFwdWaves * 64;
-  out->lds_bytes = 2 * (fa::kFwdBC * d * 2 + d * fa::kFwdBC * 2);
+  out->lds_bytes = fa::fwd_lds_bytes(d);
   out->workgroups = (int64_t)B * H * q_tiles;
   int64_t visited = 0, masked = 0;
   for (int qt = 0; qt < q_tiles; ++qt) {

@@ -236,29 +236,62 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
   if (tid == 0) part_lse[out] = (M + __log2f(L2)) * kLn2;
 }
 
+constexpr int kCombineThreads = 256;
+constexpr int kMaxSplits = 4096;  // the host rejects larger split counts
+
+// Block-wide max / sum over kCombineThreads threads (4 wavefronts).
+template <bool MAX>
+__device__ __forceinline__ float block_reduce(float x, float* red) {
+  for (int off = 32; off > 0; off >>= 1) {
+    const float y = __shfl_xor(x, off);
+    x = MAX ? fmaxf(x, y) : x + y;
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __syncthreads();
+  if (lane == 0) red[wave] = x;
+  __syncthreads();
+  x = red[0];
+  for (int w = 1; w < kCombineThreads / 64; ++w) x = MAX ? fmaxf(x, red[w]) : x + red[w];
+  return x;
+}
+
 template <int D>
-__global__ __launch_bounds__(D) void decode_combine_kernel(const float* __restrict__ part_o,
-                                                           const float* __restrict__ part_lse,
-                                                           __bf16* __restrict__ og,
-                                                           float* __restrict__ lse_out, int H,
-                                                           int S) {
+__global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(
+    const float* __restrict__ part_o, const float* __restrict__ part_lse, __bf16* __restrict__ og,
+    float* __restrict__ lse_out, int H, int S) {
+  __shared__ float w[kMaxSplits];
+  __shared__ float red[kCombineThreads / 64];
+  __shared__ float osum[kCombineThreads];
   const int h = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
   const size_t bh = (size_t)b * H + h;
   const size_t base = bh * S;
+
   float M = -INFINITY;
-  for (int k = 0; k < S; ++k) M = fmaxf(M, part_lse[base + k]);
-  float o = 0.f, sw = 0.f;
-  if (M != -INFINITY) {
-    for (int k = 0; k < S; ++k) {
-      const float lk = part_lse[base + k];
-      const float w = (lk == -INFINITY) ? 0.f : __expf(lk - M);
-      sw += w;
-      o = __builtin_fmaf(w, part_o[(base + k) * D + t], o);
-    }
-    o /= sw;
+  for (int k = t; k < S; k += kCombineThreads) M = fmaxf(M, part_lse[base + k]);
+  M = block_reduce<true>(M, red);
+  float sw = 0.f;
+  for (int k = t; k < S; k += kCombineThreads) {
+    const float lk = part_lse[base + k];
+    const float wk = (M == -INFINITY || lk == -INFINITY) ? 0.f : __expf(lk - M);
+    w[k] = wk;
+    sw += wk;
   }
-  og[bh * D + t] = (__bf16)o;
-  if (lse_out != nullptr && t == 0) lse_out[bh] = (M == -INFINITY) ? -INFINITY : M + __logf(sw);
+  sw = block_reduce<false>(sw, red);  // its barriers also publish w[]
+
+  // column t % D, partials k = t / D, t / D + 256 / D, ...
+  constexpr int kGroups = kCombineThreads / D;
+  const int col = t % D;
+  float o = 0.f;
+  for (int k = t / D; k < S; k += kGroups) o = __builtin_fmaf(w[k], part_o[(base + k) * D + col], o);
+  osum[t] = o;
+  __syncthreads();
+  if (t < D) {
+    float acc = osum[t];
+#pragma unroll
+    for (int gi = 1; gi < kGroups; ++gi) acc += osum[t + gi * D];
+    og[bh * D + t] = (__bf16)(sw > 0.f ? acc / sw : 0.f);
+    if (lse_out != nullptr && t == 0) lse_out[bh] = (M == -INFINITY) ? -INFINITY : M + __logf(sw);
+  }
 }
 
 template <int D>
@@ -269,7 +302,7 @@ hipError_t launch(const DecodeArgs& a, hipStream_t stream) {
                      a.capacity, a.scale);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(a.H, a.B), dim3(D), 0, stream, a.part_o,
+  hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(a.H, a.B), dim3(kCombineThreads), 0, stream, a.part_o,
                      a.part_lse, static_cast<__bf16*>(a.o), a.lse_out, a.H, a.S);
   return hipGetLastError();
 }

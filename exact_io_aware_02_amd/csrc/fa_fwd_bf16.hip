@@ -10,29 +10,38 @@
 // ("Infra: Flash Attention", causal figure; lecture notes section 4.3).
 //
 // Mapping onto CDNA4:
-//  * 4 wavefronts per workgroup, 32 query rows each (split-Q across
+//  * 8 wavefronts per workgroup, 32 query rows each (split-Q across
 //    wavefronts, the work split of the FlashAttention-2 section of the blog):
 //    the wavefronts share each K/V tile through LDS and never exchange
-//    partial outputs.
-//  * Scores are formed transposed, S^T = K_j Q_i^T, with
+//    partial outputs.  One workgroup per compute unit, two wavefronts per
+//    SIMD.
+//  * Scores are formed transposed, S^T = K_j Q_i^T, on
 //    v_mfma_f32_32x32x16_bf16.  In the 32x32 accumulator layout a lane holds
 //    one query column and 16 key rows, so the softmax reductions along keys
-//    are 31 in-lane max/add operations plus one exchange between lanes l and
-//    l^32 (which hold the two key halves of the same query).
+//    are in-lane (v_max3_f32 chains and fp32 adds) plus one v_permlane32_swap
+//    (lanes l and l^32 hold the two key halves of the same query).
 //  * The probabilities W leave the score accumulator already in the
 //    B-operand layout of the second product U^T += V_j^T W^T, so W never
-//    goes through LDS.  V_j is staged in LDS transposed (d-major) with its
-//    keys permuted to match the accumulator's register order, so each
-//    A-operand fragment is one 16-byte LDS read.
-//  * U^T lives in the accumulator layout with the query on the lane, so the
-//    rescale by alpha is one multiply per register with a per-lane scalar;
-//    it is skipped when no row of the wavefront raised its maximum (alpha is
-//    then exactly 1).
-//  * Exponentials run in base 2: scale*log2(e) is folded into one FMA per
-//    score before v_exp_f32.
-//  * K/V tiles are double-buffered in LDS: the next tile's global loads are
-//    in flight while the current tile is computed.  16-byte LDS chunks are
-//    XOR-swizzled so the 16-byte reads and writes are bank-conflict free.
+//    goes through LDS.  The matching A operand (8 keys of one head dimension
+//    per lane) is assembled by two transposing LDS reads (ds_read_b64_tr_b16).
+//  * Q (read once per workgroup), K and V go from HBM to LDS with direct
+//    buffer->LDS loads (no staging registers; rows past N read as zeros).
+//    LDS rows are padded by 16 bytes, and V rows are stored in a permuted
+//    order, so that every LDS read of the loop (16-byte K and Q fragments,
+//    transposing V reads) is free of bank conflicts and addressed by one
+//    per-lane base register plus a compile-time offset.
+//  * Software pipeline: while the softmax of tile j runs on the VALU, the
+//    score MFMAs of tile j+1 are issued from the same wavefront; K tiles are
+//    loaded two tiles ahead and V tiles one tile ahead, with one barrier per
+//    tile.
+//  * U^T lives in the accumulator layout with the query on the lane, so a
+//    rescale by alpha is one multiply per register.  Rescaling is
+//    conditional ("Infra: Flash Attention", section "Invariant of
+//    conditional rescaling"): the base r of a row moves only when the tile
+//    maximum exceeds it by more than 8 in the base-2 exponent, so W <= 2^8;
+//    l, U and the new tile always share the same base and the final U / l is
+//    unchanged.  Exponentials run in base 2 with scale*log2(e) folded into
+//    one FMA per score.
 //  * Workgroup ids are remapped so that all query tiles of one head run on
 //    the same XCD (dispatch is round-robin over the 8 XCDs), letting the
 //    head's K/V re-reads hit that XCD's L2; causal launches take the longest
@@ -44,46 +53,63 @@ namespace fa {
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 
+#define LDS_AS __attribute__((address_space(3)))
+
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kRescaleLog2 = 8.f;  // conditional-rescale threshold (base-2 exponent)
 constexpr int kThreads = kFwdWaves * 64;
+
+// Tuning knobs (compile-time).
+#ifndef FA_FWD_INTERLEAVE
+#define FA_FWD_INTERLEAVE 6  // VALU instructions placed after each score MFMA (0 = compiler's choice)
+#endif
 
 template <int D>
 struct Tile {
-  static constexpr int kChunks = D / 8;                    // 16-byte chunks per K row
-  static constexpr int kKBytes = kFwdBC * D * 2;           // K tile [BC][D]
-  static constexpr int kVtRowBytes = kFwdBC * 2;           // Vt row: BC keys
-  static constexpr int kVBytes = D * kVtRowBytes;          // Vt tile [D][BC]
-  static constexpr int kBufBytes = kKBytes + kVBytes;
-  static constexpr int kKLoads = kFwdBC * kChunks / kThreads;  // 16B loads per thread
-  static constexpr int kKeysPerThreadV = kKLoads;              // V: keys per thread
-  static_assert(kKLoads * kThreads == kFwdBC * kChunks, "tile/thread mismatch");
+  static constexpr int kRowBytes = D * 2;
+  static constexpr int kStride = kRowBytes + 16;           // padded LDS row
+  static constexpr int kChunks = D / 8;                    // 16-byte chunks per row
+  static constexpr int kBytes = kFwdBC * kStride;          // one K or V tile in LDS
+  static constexpr int kLoads = kBytes / 1024;             // 1 KiB buffer->LDS loads per tile
+  static constexpr int kQBytes = kFwdBR * kStride;
+  static constexpr int kQLoads = kQBytes / 1024;
+  static constexpr int kLdsBytes = kQBytes + 4 * kBytes;   // Q, K x2, V x2
+  static constexpr int kLoadsPerWave = (kLoads + kFwdWaves - 1) / kFwdWaves;
+  static constexpr int kQLoadsPerWave = (kQLoads + kFwdWaves - 1) / kFwdWaves;
+  static_assert(kLoads * 1024 == kBytes && kQLoads * 1024 == kQBytes, "padded tiles must be whole KiB");
+  static_assert(kLdsBytes == fwd_lds_bytes(D), "LDS size must match the planner");
 };
 
-// Byte offset of 16-byte chunk `c` of K row `r` (XOR swizzle on r mod 8).
-template <int D>
-__device__ __forceinline__ int k_off(int r, int c) {
-  return r * (D * 2) + ((c ^ (r & 7)) << 4);
+// V rows are stored with the two 2-bit fields of (key mod 16) swapped, so
+// the 4 consecutive keys of one transposing read land 4 rows apart.
+__host__ __device__ constexpr int vrow_perm(int k) {
+  return (k & ~15) | ((k & 3) << 2) | ((k >> 2) & 3);
 }
 
-// Byte offset of 16-byte chunk `c` of Vt row `dr`.  The swizzle mixes bits of
-// dr and dr/8 so that both the reads (32 consecutive rows, same chunk) and
-// the transposing writes (rows 8 apart, same chunk) spread over banks.
-__device__ __forceinline__ int vt_off(int dr, int c) {
-  return dr * (kFwdBC * 2) + ((c ^ ((dr ^ (dr >> 3)) & 7)) << 4);
-}
+template <bool B>
+struct BoolTag {
+  static constexpr bool value = B;
+};
+template <int I>
+struct IntTag {
+  static constexpr int value = I;
+};
 
-// Position of key `k` inside a Vt row.  Within every group of 16 keys the
-// second and third runs of 4 are swapped, which makes the 8 keys that one
-// lane group feeds to one W^T V^T k-step contiguous.
-__device__ __forceinline__ int vt_pos(int k) {
-  int q4 = (k >> 2) & 3;
-  int q4p = ((q4 & 1) << 1) | (q4 >> 1);
-  return (k & ~15) | (q4p << 2) | (k & 3);
+// Buffer resource over `bytes` bytes at `base`; loads at offsets past the end
+// return zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, unsigned bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+// 16 bytes per lane from rsrc[voff + soff] into LDS at lds + 16 * lane.
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rsrc, void LDS_AS* lds, unsigned voff,
+                                           unsigned soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, lds, 16, voff, soff, 0, 0);
 }
 
 __device__ __forceinline__ unsigned pack_bf16x2(float a, float b) {
@@ -91,8 +117,31 @@ __device__ __forceinline__ unsigned pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(unsigned, v);
 }
 
-// Value held by lane l^32 (the other key half of the same query).
-__device__ __forceinline__ float swap32(float x) { return __shfl_xor(x, 32); }
+// max / sum with lane l^32 (the other key half of the same query); the swap
+// returns (x[l & 31], x[32 + (l & 31)]) in every lane.
+__device__ __forceinline__ float pair_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Buffer offset of the 16 bytes that belong at byte `o` of a padded LDS tile;
+// a padding slot gets an offset past any buffer end (reads as zero, touches
+// no memory).
+template <int D>
+__device__ __forceinline__ unsigned lds_slot_source(int o, bool permuted) {
+  using T = Tile<D>;
+  const int p = o / T::kStride;
+  const int ch = (o - p * T::kStride) >> 4;
+  if (ch >= T::kChunks) return 0xFFFFFFF0u;
+  const int row = permuted ? vrow_perm(p) : p;
+  return (unsigned)(row * T::kRowBytes + ch * 16);
+}
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -100,11 +149,12 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ K
                      const __bf16* __restrict__ Vg, __bf16* __restrict__ Og,
                      float* __restrict__ Lg, int N, int q_tiles, float scale) {
   using T = Tile<D>;
-  __shared__ __attribute__((aligned(16))) char smem[2 * T::kBufBytes];
+  // [Q tile][K buffer 0][K buffer 1][V buffer 0][V buffer 1], padded rows
+  __shared__ __attribute__((aligned(1024))) char smem[T::kLdsBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31;
   const int g = lane >> 5;  // lane group: which 8-wide k slice a lane feeds
 
@@ -119,10 +169,6 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ K
   const int qt = CAUSAL ? (q_tiles - 1 - qi) : qi;
 
   const size_t head_off = (size_t)bh * N * D;
-  const __bf16* Qh = Qg + head_off;
-  const __bf16* Kh = Kg + head_off;
-  const __bf16* Vh = Vg + head_off;
-
   const int q0 = qt * kFwdBR;
   const int qw0 = q0 + wave * 32;  // first query row of this wavefront
   const int qrow = qw0 + l32;      // the query this lane's column belongs to
@@ -134,178 +180,219 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ K
     n_tiles = min(n_tiles, last / kFwdBC + 1);
   }
 
-  // ---- Q fragments (B operand of S^T = K Q^T), kept in registers
-  bf16x8_t qf[D / 16];
+  char LDS_AS* lds = (char LDS_AS*)smem;
+  char LDS_AS* qlds = lds;
+  auto kbuf = [&](int s) { return lds + T::kQBytes + s * T::kBytes; };
+  auto vbuf = [&](int s) { return lds + T::kQBytes + (2 + s) * T::kBytes; };
+
+  // ---- buffer -> LDS loads (voffsets fixed per lane, tile offset scalar)
+  const unsigned head_bytes = (unsigned)N * D * 2;
+  const __amdgpu_buffer_rsrc_t k_rsrc = make_rsrc(Kg + head_off, head_bytes);
+  const __amdgpu_buffer_rsrc_t v_rsrc = make_rsrc(Vg + head_off, head_bytes);
+  unsigned k_voff[T::kLoadsPerWave], v_voff[T::kLoadsPerWave];
 #pragma unroll
-  for (int ds = 0; ds < D / 16; ++ds) {
-    if (qrow < N) {
-      qf[ds] = *reinterpret_cast<const bf16x8_t*>(Qh + (size_t)qrow * D + ds * 16 + g * 8);
-    } else {
-      qf[ds] = bf16x8_t{};
-    }
+  for (int p = 0; p < T::kLoadsPerWave; ++p) {
+    const int o = (wave + p * kFwdWaves) * 1024 + lane * 16;
+    k_voff[p] = lds_slot_source<D>(o, false);
+    v_voff[p] = lds_slot_source<D>(o, true);
   }
+  auto dma_tile = [&](__amdgpu_buffer_rsrc_t rsrc, const unsigned* voff, int tile, char LDS_AS* dst) {
+    const unsigned soff = (unsigned)tile * kFwdBC * T::kRowBytes;
+#pragma unroll
+    for (int p = 0; p < T::kLoadsPerWave; ++p) {
+      const int blk = wave + p * kFwdWaves;
+      if (p + 1 < T::kLoadsPerWave || blk < T::kLoads)
+        load_lds16(rsrc, (void LDS_AS*)(dst + blk * 1024), voff[p], soff);
+    }
+  };
 
-  // ---- staging registers for the next K/V tile
-  u32x4_t kreg[T::kKLoads];
-  u32x4_t vreg[T::kKeysPerThreadV];
-  const int kc = tid % T::kChunks;  // chunk column this thread loads
-  const int krow0 = tid / T::kChunks;
-  constexpr int kRowsPerPass = kThreads / T::kChunks;
-  const int vkey0 = (tid / T::kChunks) * T::kKeysPerThreadV;  // first of this thread's V keys
+  // ---- per-lane LDS read bases (everything else is a compile-time offset)
+  // K / Q fragment (A / B operand of S^T = K Q^T): row l32, chunk 2*ds + g
+  const int kq_base = l32 * T::kStride + g * 16;
+  const int q_base = kq_base + wave * 32 * T::kStride;
+  // V^T fragment for key step ks, half t: keys ks*16 + 8t + 4g + k (k = 0..3)
+  // at stored rows ks*16 + 4k + 2t + g; lanes address dims 16*((lane>>4)&1) + 4*(lane&3)
+  const int v_base = (4 * ((lane & 15) >> 2) + g) * T::kStride +
+                     (((lane >> 4) & 1) * 16 + (lane & 3) * 4) * 2;
 
-  auto load_tile = [&](int j) {
+  // S^T tile from the K tile at `kb`: d-steps [DS0, DS1) of the contraction
+  // (DS0 == 0 starts the accumulation)
+  auto scores = [&](const char LDS_AS* kb, f32x16_t& s0, f32x16_t& s1, auto ds0_tag, auto ds1_tag) {
+    constexpr int DS0 = decltype(ds0_tag)::value, DS1 = decltype(ds1_tag)::value;
+    if constexpr (DS0 == 0) {
+      s0 = f32x16_t{};
+      s1 = f32x16_t{};
+    }
+#pragma unroll
+    for (int ds = DS0; ds < DS1; ++ds) {
+      const bf16x8_t qf = *(const bf16x8_t LDS_AS*)(qlds + q_base + ds * 32);
+      const bf16x8_t a0 = *(const bf16x8_t LDS_AS*)(kb + kq_base + ds * 32);
+      const bf16x8_t a1 = *(const bf16x8_t LDS_AS*)(kb + kq_base + 32 * T::kStride + ds * 32);
+      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf, s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf, s1, 0, 0, 0);
+    }
+  };
+
+  auto needs_mask = [&](int j) {
     const int kbase = j * kFwdBC;
+    return (kbase + kFwdBC > N) || (CAUSAL && kbase + kFwdBC - 1 > qw0);
+  };
+  // keys past N, and keys after the query when causal, get -inf
+  auto apply_mask = [&](int j, f32x16_t& s0, f32x16_t& s1) {
+    const int kbase = j * kFwdBC;
+    const int lim = CAUSAL ? min(N - 1, qrow) : N - 1;  // last valid key
 #pragma unroll
-    for (int p = 0; p < T::kKLoads; ++p) {
-      int r = kbase + krow0 + p * kRowsPerPass;
-      kreg[p] = (r < N) ? *reinterpret_cast<const u32x4_t*>(Kh + (size_t)r * D + kc * 8) : u32x4_t{};
-    }
-#pragma unroll
-    for (int p = 0; p < T::kKeysPerThreadV; ++p) {
-      int r = kbase + vkey0 + p;
-      vreg[p] = (r < N) ? *reinterpret_cast<const u32x4_t*>(Vh + (size_t)r * D + kc * 8) : u32x4_t{};
+    for (int i = 0; i < 16; ++i) {
+      const int kr = kbase + 8 * (i >> 2) + 4 * g + (i & 3);
+      if (kr > lim) s0[i] = -INFINITY;
+      if (kr + 32 > lim) s1[i] = -INFINITY;
     }
   };
 
-  auto store_tile = [&](int buf) {
-    char* kb = smem + buf * T::kBufBytes;
-    char* vb = kb + T::kKBytes;
+  auto v_frag = [&](const char LDS_AS* vb, int db, int ks) {
+    bf16x8_t a;
 #pragma unroll
-    for (int p = 0; p < T::kKLoads; ++p) {
-      int r = krow0 + p * kRowsPerPass;
-      *reinterpret_cast<u32x4_t*>(kb + k_off<D>(r, kc)) = kreg[p];
+    for (int t = 0; t < 2; ++t) {
+      const char LDS_AS* p = vb + v_base + (ks * 16 + 2 * t) * T::kStride + db * 64;
+      const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4_t LDS_AS*)p);
+      const bf16x4_t vb4 = __builtin_bit_cast(bf16x4_t, v);
+      a[4 * t + 0] = vb4[0];
+      a[4 * t + 1] = vb4[1];
+      a[4 * t + 2] = vb4[2];
+      a[4 * t + 3] = vb4[3];
     }
-    // transpose: thread holds keys vkey0.. (kKeysPerThreadV of them) x 8 dims
-    const int pos = vt_pos(vkey0);
-    const int cpos = pos >> 3;              // 16B chunk within the Vt row
-    const int bpos = (pos & 7) * 2;         // byte within the chunk
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int dr = kc * 8 + e;
-      char* dst = vb + vt_off(dr, cpos) + bpos;
-      const int w = e >> 1;
-      if constexpr (T::kKeysPerThreadV == 4) {
-        unsigned a0 = vreg[0][w], a1 = vreg[1][w], a2 = vreg[2][w], a3 = vreg[3][w];
-        u32x2_t out;
-        if (e & 1) {
-          out[0] = (a0 >> 16) | (a1 & 0xffff0000u);
-          out[1] = (a2 >> 16) | (a3 & 0xffff0000u);
-        } else {
-          out[0] = (a0 & 0xffffu) | (a1 << 16);
-          out[1] = (a2 & 0xffffu) | (a3 << 16);
-        }
-        *reinterpret_cast<u32x2_t*>(dst) = out;
-      } else {
-        unsigned a0 = vreg[0][w], a1 = vreg[1][w];
-        unsigned out = (e & 1) ? ((a0 >> 16) | (a1 & 0xffff0000u)) : ((a0 & 0xffffu) | (a1 << 16));
-        *reinterpret_cast<unsigned*>(dst) = out;
-      }
-    }
+    return a;
   };
 
-  // ---- online-softmax state: m (raw score units, same in lanes l, l^32),
-  // per-lane partial l over the lane's own keys, and U^T accumulators.
+  // ---- online-softmax state: base m (raw score units, equal in lanes l and
+  // l^32), per-lane partial l over the lane's keys, and U^T accumulators.
   const float c = scale * kLog2e;
-  float m_run = -INFINITY;
+  const float theta = kRescaleLog2 / c;  // threshold in raw score units
+  float m_ref = -INFINITY;
   float l_run = 0.f;
   f32x16_t u[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) u[db] = f32x16_t{};
 
-  load_tile(0);
-  store_tile(0);
+  // ---- prologue: Q, K_0, V_0, K_1 in flight; S_0
+  {
+    const __amdgpu_buffer_rsrc_t q_rsrc = make_rsrc(Qg + head_off, head_bytes);
+    const unsigned q_soff = (unsigned)q0 * T::kRowBytes;
+#pragma unroll
+    for (int p = 0; p < T::kQLoadsPerWave; ++p) {
+      const int blk = wave + p * kFwdWaves;
+      if (blk < T::kQLoads)
+        load_lds16(q_rsrc, (void LDS_AS*)(qlds + blk * 1024),
+                   lds_slot_source<D>(blk * 1024 + lane * 16, false), q_soff);
+    }
+  }
+  dma_tile(k_rsrc, k_voff, 0, kbuf(0));
+  dma_tile(v_rsrc, v_voff, 0, vbuf(0));
+  if (n_tiles > 1) dma_tile(k_rsrc, k_voff, 1, kbuf(1));
+  wait_vmem();
   __syncthreads();
+  f32x16_t sc0, sc1, sn0, sn1;  // scores of two consecutive tiles
+  scores(kbuf(0), sc0, sc1, IntTag<0>{}, IntTag<D / 16>{});
+  if (needs_mask(0)) apply_mask(0, sc0, sc1);
 
-  for (int j = 0; j < n_tiles; ++j) {
-    const int buf = j & 1;
-    if (j + 1 < n_tiles) load_tile(j + 1);
+  // one KV tile: s0/s1 hold its (masked) scores; with HAS_NEXT the scores
+  // of the next tile are accumulated into n0/n1 meanwhile
+  auto step = [&](int j, f32x16_t& s0, f32x16_t& s1, f32x16_t& n0, f32x16_t& n1,
+                  auto has_next_tag) {
+    constexpr bool HAS_NEXT = decltype(has_next_tag)::value;
+    constexpr int kSplit = 2;  // d-steps of the next tile issued before the rescale branch
+    wait_vmem();
+    __syncthreads();
+    if (j + 2 < n_tiles) dma_tile(k_rsrc, k_voff, j + 2, kbuf(j & 1));
+    if (HAS_NEXT) dma_tile(v_rsrc, v_voff, j + 1, vbuf((j + 1) & 1));
+    const char LDS_AS* knext = kbuf((j + 1) & 1);
 
-    const int kbase = j * kFwdBC;
-    // a wavefront whose every row lies before this tile's first key has
-    // nothing to add (all its rows are fully masked here): skip the update
-    const bool wave_live = !CAUSAL || (kbase <= qw0 + 31);
+    if constexpr (HAS_NEXT) scores(knext, n0, n1, IntTag<0>{}, IntTag<kSplit>{});
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mx = fmaxf(fmaxf(mx, s0[i]), s1[i]);
+    mx = pair_max(mx);
+    // move the base only if the tile max exceeds it by more than the
+    // threshold (always on the first tile with a valid key)
+    const float m_new = (mx > m_ref + theta) ? mx : m_ref;
+    const float mc = (m_new == -INFINITY) ? 0.f : m_new * c;
+    const bool moved = m_new > m_ref;
+    const float alpha = moved ? __builtin_amdgcn_exp2f(m_ref * c - mc) : 1.f;
+    m_ref = m_new;
+    if (__any(moved)) {
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) u[db] *= alpha;
+    }
+
+    // softmax of tile j (VALU) overlapped with the rest of the score MFMAs
+    // of tile j+1.  The row sum adds the fp32 weights, so l (and L) carry no
+    // bf16 rounding; only the W V product sees bf16 weights.
+    if constexpr (HAS_NEXT) scores(knext, n0, n1, IntTag<kSplit>{}, IntTag<D / 16>{});
+    bf16x8_t wb[4];
+    float rs = 0.f;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      float p[8], q[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        p[t] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[8 * h + t], c, -mc));
+        q[t] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[8 * h + t], c, -mc));
+        rs += p[t] + q[t];
+      }
+      wb[h] = bf16x8_t{(__bf16)p[0], (__bf16)p[1], (__bf16)p[2], (__bf16)p[3],
+                       (__bf16)p[4], (__bf16)p[5], (__bf16)p[6], (__bf16)p[7]};
+      wb[2 + h] = bf16x8_t{(__bf16)q[0], (__bf16)q[1], (__bf16)q[2], (__bf16)q[3],
+                           (__bf16)q[4], (__bf16)q[5], (__bf16)q[6], (__bf16)q[7]};
+    }
+    l_run = alpha * l_run + rs;
+#if FA_FWD_INTERLEAVE > 0
+    if constexpr (HAS_NEXT) {
+      // one score MFMA with its fragment reads, then a run of softmax VALU
+#pragma unroll
+      for (int i = 0; i < D / 16 - kSplit; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, FA_FWD_INTERLEAVE, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, FA_FWD_INTERLEAVE, 0);
+      }
+    }
+#endif
+
+    // U^T += V_j^T W^T (a wavefront with every row before this tile's first
+    // key has only zero weights here: skip it)
+    const bool wave_live = !CAUSAL || (j * kFwdBC <= qw0 + 31);
     if (wave_live) {
-      const char* kb = smem + buf * T::kBufBytes;
-      const char* vb = kb + T::kKBytes;
-
-      // S^T (keys x queries) for the two 32-key halves of the tile
-      f32x16_t s0 = f32x16_t{}, s1 = f32x16_t{};
-#pragma unroll
-      for (int ds = 0; ds < D / 16; ++ds) {
-        bf16x8_t a0 = *reinterpret_cast<const bf16x8_t*>(kb + k_off<D>(l32, 2 * ds + g));
-        bf16x8_t a1 = *reinterpret_cast<const bf16x8_t*>(kb + k_off<D>(32 + l32, 2 * ds + g));
-        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[ds], s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[ds], s1, 0, 0, 0);
-      }
-
-      // mask: keys past N, and keys after the query when causal
-      const bool need_mask = (kbase + kFwdBC > N) || (CAUSAL && kbase + kFwdBC - 1 > qw0);
-      if (need_mask) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int kr = 8 * (i >> 2) + 4 * g + (i & 3);
-          const int k0 = kbase + kr, k1 = kbase + 32 + kr;
-          if (k0 >= N || (CAUSAL && k0 > qrow)) s0[i] = -INFINITY;
-          if (k1 >= N || (CAUSAL && k1 > qrow)) s1[i] = -INFINITY;
-        }
-      }
-
-      // row max over the tile's keys: in-lane, then across the lane pair
-      float mx = fmaxf(s0[0], s1[0]);
-#pragma unroll
-      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(s0[i], s1[i]));
-      mx = fmaxf(mx, swap32(mx));
-      const float m_new = fmaxf(m_run, mx);
-      // a row with no valid key so far keeps m = -inf: use base 0 so no
-      // -inf - (-inf) is formed; its weights are exp2(-inf) = 0
-      const float mc = (m_new == -INFINITY) ? 0.f : m_new * c;
-      const bool raised = m_new > m_run;
-      const float alpha = raised ? __builtin_amdgcn_exp2f(m_run * c - mc) : 1.f;
-
-      // W = exp2(S*c - m'*c), row sums, and the bf16 B operands of W^T
-      bf16x8_t wb[4];
-      float rs = 0.f;
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        float p[8], q[8];
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          p[t] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[8 * h + t], c, -mc));
-          q[t] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[8 * h + t], c, -mc));
-          rs += p[t] + q[t];
-        }
-        wb[h] = bf16x8_t{(__bf16)p[0], (__bf16)p[1], (__bf16)p[2], (__bf16)p[3],
-                         (__bf16)p[4], (__bf16)p[5], (__bf16)p[6], (__bf16)p[7]};
-        wb[2 + h] = bf16x8_t{(__bf16)q[0], (__bf16)q[1], (__bf16)q[2], (__bf16)q[3],
-                             (__bf16)q[4], (__bf16)q[5], (__bf16)q[6], (__bf16)q[7]};
-      }
-      l_run = alpha * l_run + rs;
-
-      // U = alpha U, skipped when no row of the wavefront raised its max
-      if (__any(raised)) {
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) u[db] *= alpha;
-      }
-
-      // U^T += V^T W^T: k-steps of 16 keys, kstep = 2*kb + h
+      const char LDS_AS* vb = vbuf(j & 1);
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) {
-        const int dr = db * 32 + l32;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-          bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(vb + vt_off(dr, 2 * ks + g));
+          const bf16x8_t a = v_frag(vb, db, ks);
           u[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, wb[ks], u[db], 0, 0, 0);
         }
       }
-      m_run = m_new;
     }
+    if constexpr (HAS_NEXT) {
+      if (needs_mask(j + 1)) apply_mask(j + 1, n0, n1);
+    }
+  };
 
-    if (j + 1 < n_tiles) store_tile(buf ^ 1);
-    __syncthreads();
+  // two tiles per trip so the score registers alternate without copies
+  int j = 0;
+  for (; j + 2 < n_tiles; j += 2) {
+    step(j, sc0, sc1, sn0, sn1, BoolTag<true>{});
+    step(j + 1, sn0, sn1, sc0, sc1, BoolTag<true>{});
+  }
+  if (j + 1 < n_tiles) {
+    step(j, sc0, sc1, sn0, sn1, BoolTag<true>{});
+    step(j + 1, sn0, sn1, sc0, sc1, BoolTag<false>{});
+  } else {
+    step(j, sc0, sc1, sn0, sn1, BoolTag<false>{});
   }
 
   // ---- epilogue: O = U / l, L = m * scale + ln l
-  const float l_tot = l_run + swap32(l_run);
+  const float l_tot = pair_sum(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (qrow < N) {
     __bf16* orow = Og + head_off + (size_t)qrow * D;
@@ -321,7 +408,7 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ K
       }
     }
     if (Lg != nullptr && g == 0) {
-      Lg[(size_t)bh * N + qrow] = l_tot > 0.f ? m_run * scale + __logf(l_tot) : -INFINITY;
+      Lg[(size_t)bh * N + qrow] = l_tot > 0.f ? m_ref * scale + __logf(l_tot) : -INFINITY;
     }
   }
 }

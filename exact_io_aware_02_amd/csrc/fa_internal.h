@@ -10,9 +10,12 @@ namespace fa {
 // Prefill tiling, shared by the planner and the bf16 kernel: a workgroup of
 // kFwdWaves wavefronts owns kFwdBR query rows (32 per wavefront) and walks
 // KV tiles of kFwdBC keys.
-constexpr int kFwdWaves = 4;
+constexpr int kFwdWaves = 8;
 constexpr int kFwdBR = 32 * kFwdWaves;
 constexpr int kFwdBC = 64;
+// LDS of one prefill workgroup: the query tile and two K and two V tiles,
+// each row padded by 16 bytes.
+__host__ __device__ constexpr int fwd_lds_bytes(int d) { return (kFwdBR + 4 * kFwdBC) * (2 * d + 16); }
 
 // fp32 prefill: one wavefront, one query row per lane, 64-key tiles.
 constexpr int kF32BR = 64;

@@ -108,8 +108,8 @@ int fa_fwd_f32(const float* Q, const float* K, const float* V, float* O, float* 
  *   o       : device bf16 [B, H, d]
  *   Lkv     : device int32 [B], per-sequence cache lengths (>= 0).  A length
  *             of 0 gives o = 0 for that sequence.
- *   num_splits : chunks per (b, h); 0 = automatic (from the device's compute
- *             unit count and B * H).  Sequence b is cut into chunks of
+ *   num_splits : chunks per (b, h); 0 = automatic: ceil(CUs / (B * H))
+ *             clamped to [8, 256], CUs being the device's compute units.  Sequence b is cut into chunks of
  *             ceil(Lkv[b] / num_splits) tokens rounded up to a multiple of 64;
  *             trailing chunks may be empty.
  * The query attends to every cached key with scale 1/sqrt(d).  Partials go to

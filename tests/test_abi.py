@@ -134,9 +134,12 @@ def test_decode_workspace_formula():
         assert p["num_splits"] == S and p["split_workgroups"] == B * H * S
         assert p["workspace_bytes"] == fa.fa_decode_workspace_bytes(B, H, d, S)
     assert fa.fa_decode_workspace_bytes(0, 1, 128, 1) == 0
-    # automatic split count, planned for a 256-CU device: about 8 workgroups per CU
-    assert fa.fa_decode_plan(1, 32, 128, 0)["num_splits"] == 64
+    # automatic split count, planned for a 256-CU device: cover every CU once,
+    # with at least 8 chunks per sequence
+    assert fa.fa_decode_plan(1, 32, 128, 0)["num_splits"] == 8
     assert fa.fa_decode_plan(8, 32, 128, 0)["num_splits"] == 8
+    assert fa.fa_decode_plan(1, 4, 128, 0)["num_splits"] == 64
+    assert fa.fa_decode_plan(1, 1, 128, 0)["num_splits"] == 256
 
 
 @pytest.mark.parametrize("L", [1, 63, 64, 65, 511, 512, 4096, 32768, 65536, 40001])
@@ -157,22 +160,25 @@ def test_decode_chunks_cover_every_key_once(L, S):
 @pytest.mark.parametrize("causal", [0, 1])
 @pytest.mark.parametrize("N", [1, 64, 100, 128, 129, 1000, 2048])
 def test_fwd_plan_tile_count_matches_oracle(N, causal):
-    """The tiles fa_fwd visits are those of Algorithm 1 with B_r = 128,
-    B_c = 64 and whole-tile causal skipping, as counted by the oracle."""
+    """The tiles fa_fwd visits are those of Algorithm 1 with the kernel's
+    B_r, B_c and whole-tile causal skipping, as counted by the oracle."""
     fa = _fa()
     p = fa.fa_fwd_plan(2, 3, N, 128, causal)
     rng = np.random.default_rng(0)
     Q, K, V = (rng.standard_normal((N, 2)) for _ in range(3))
     _, _, cnt = oracle.tiled_ref(Q, K, V, p["block_rows"], p["block_cols"], 1.0, causal=bool(causal), count=True)
     assert p["tiles_visited"] == 6 * cnt["tiles"]
-    assert p["workgroups"] == 6 * -(-N // 128)
+    assert p["workgroups"] == 6 * -(-N // p["block_rows"])
 
 
 def test_fwd_plan_causal_pin_exercise4():
     """With square tiles the causal count is T(T+1)/2 ('CMU 10-423 Lecture
-    18', Exercise 4); with B_r = 2 B_c each query tile covers two KV tiles,
-    so the count at N = 4096 is 2 * 32*33/2 per head."""
+    18', Exercise 4); with B_r = r B_c each query tile covers r KV tiles per
+    query-tile step, so the count is r * T(T+1)/2 with T = N / B_r."""
     fa = _fa()
-    p = fa.fa_fwd_plan(1, 1, 4096, 128, 1)
-    assert p["tiles_visited"] == 2 * oracle.causal_tile_count(32)
-    assert fa.fa_fwd_plan(1, 1, 4096, 128, 0)["tiles_visited"] == 32 * 64
+    N = 4096
+    p = fa.fa_fwd_plan(1, 1, N, 128, 1)
+    r = p["block_rows"] // p["block_cols"]
+    T = N // p["block_rows"]
+    assert p["tiles_visited"] == r * oracle.causal_tile_count(T)
+    assert fa.fa_fwd_plan(1, 1, N, 128, 0)["tiles_visited"] == T * (N // p["block_cols"])
