@@ -14,26 +14,31 @@
 //    wavefronts, the work split of the FlashAttention-2 section of the blog):
 //    the wavefronts share each K/V tile through LDS and never exchange
 //    partial outputs.  One workgroup per compute unit, two wavefronts per
-//    SIMD.
+//    SIMD (wavefronts w and w+4 share a SIMD).
+//  * Q is read once, straight from HBM into registers, already in the
+//    operand layout of the score product; LDS holds only K and V tiles
+//    (double-buffered, kFwdBC keys each).
 //  * Scores are formed transposed, S^T = K_j Q_i^T, on
 //    v_mfma_f32_32x32x16_bf16.  In the 32x32 accumulator layout a lane holds
-//    one query column and 16 key rows, so the softmax reductions along keys
-//    are in-lane (v_max3_f32 chains and fp32 adds) plus one v_permlane32_swap
-//    (lanes l and l^32 hold the two key halves of the same query).
+//    one query column and 16 key rows per 32-key block, so the softmax
+//    reductions along keys are in-lane (v_max3_f32 chains and fp32 adds)
+//    plus one v_permlane32_swap (lanes l and l^32 hold the two key halves of
+//    the same query).
 //  * The probabilities W leave the score accumulator already in the
 //    B-operand layout of the second product U^T += V_j^T W^T, so W never
 //    goes through LDS.  The matching A operand (8 keys of one head dimension
 //    per lane) is assembled by two transposing LDS reads (ds_read_b64_tr_b16).
-//  * Q (read once per workgroup), K and V go from HBM to LDS with direct
-//    buffer->LDS loads (no staging registers; rows past N read as zeros).
-//    LDS rows are padded by 16 bytes, and V rows are stored in a permuted
-//    order, so that every LDS read of the loop (16-byte K and Q fragments,
-//    transposing V reads) is free of bank conflicts and addressed by one
-//    per-lane base register plus a compile-time offset.
-//  * Software pipeline: while the softmax of tile j runs on the VALU, the
-//    score MFMAs of tile j+1 are issued from the same wavefront; K tiles are
-//    loaded two tiles ahead and V tiles one tile ahead, with one barrier per
-//    tile.
+//  * K and V go from HBM to LDS with direct buffer->LDS loads (no staging
+//    registers; rows past N read as zeros).  LDS rows are padded by 16 bytes,
+//    and V rows are stored in a permuted order, so that every LDS read of the
+//    loop (16-byte K fragments, transposing V reads) is free of bank
+//    conflicts and addressed by one per-lane base register plus a
+//    compile-time offset.
+//  * Ping-pong schedule: each KV tile takes two barrier-separated slots per
+//    wavefront, a softmax slot (VALU only) and a matrix slot (MFMA only: the
+//    W V product of this tile, then the scores of the next).  The two
+//    wavefronts of a SIMD run one slot apart, so the matrix core works on one
+//    wavefront's products while the other computes its exponentials.
 //  * U^T lives in the accumulator layout with the query on the lane, so a
 //    rescale by alpha is one multiply per register.  Rescaling is
 //    conditional ("Infra: Flash Attention", section "Invariant of
@@ -58,16 +63,19 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
 #define LDS_AS __attribute__((address_space(3)))
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleLog2 = 8.f;  // conditional-rescale threshold (base-2 exponent)
 constexpr int kThreads = kFwdWaves * 64;
+constexpr int kKB = kFwdBC / 32;  // 32-key blocks per KV tile (score accumulators)
+constexpr int kKS = kFwdBC / 16;  // 16-key MFMA steps per KV tile
 
-// Tuning knobs (compile-time).
-#ifndef FA_FWD_INTERLEAVE
-#define FA_FWD_INTERLEAVE 6  // VALU instructions placed after each score MFMA (0 = compiler's choice)
+// Tuning knob (compile-time).
+#ifndef FA_FWD_PINGPONG
+#define FA_FWD_PINGPONG 1  // 0: every wavefront in group 0 (lockstep slots)
 #endif
 
 template <int D>
@@ -77,12 +85,9 @@ struct Tile {
   static constexpr int kChunks = D / 8;                    // 16-byte chunks per row
   static constexpr int kBytes = kFwdBC * kStride;          // one K or V tile in LDS
   static constexpr int kLoads = kBytes / 1024;             // 1 KiB buffer->LDS loads per tile
-  static constexpr int kQBytes = kFwdBR * kStride;
-  static constexpr int kQLoads = kQBytes / 1024;
-  static constexpr int kLdsBytes = kQBytes + 4 * kBytes;   // Q, K x2, V x2
+  static constexpr int kLdsBytes = 4 * kBytes;             // K x2, V x2
   static constexpr int kLoadsPerWave = (kLoads + kFwdWaves - 1) / kFwdWaves;
-  static constexpr int kQLoadsPerWave = (kQLoads + kFwdWaves - 1) / kFwdWaves;
-  static_assert(kLoads * 1024 == kBytes && kQLoads * 1024 == kQBytes, "padded tiles must be whole KiB");
+  static_assert(kLoads * 1024 == kBytes, "padded tiles must be whole KiB");
   static_assert(kLdsBytes == fwd_lds_bytes(D), "LDS size must match the planner");
 };
 
@@ -92,24 +97,25 @@ __host__ __device__ constexpr int vrow_perm(int k) {
   return (k & ~15) | ((k & 3) << 2) | ((k >> 2) & 3);
 }
 
-template <bool B>
-struct BoolTag {
-  static constexpr bool value = B;
-};
-template <int I>
-struct IntTag {
-  static constexpr int value = I;
-};
-
-// Buffer resource over `bytes` bytes at `base`; loads at offsets past the end
-// return zeros.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, unsigned bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+// Buffer resource (4 descriptor words) over `bytes` bytes at `base`, no
+// stride; loads at offsets past the end return zeros.
+__device__ __forceinline__ u32x4_t make_rsrc(const void* base, unsigned bytes) {
+  const unsigned long long a = (unsigned long long)base;
+  return u32x4_t{(unsigned)a, (unsigned)(a >> 32) & 0xFFFFu, bytes, 0x00020000u};
 }
 // 16 bytes per lane from rsrc[voff + soff] into LDS at lds + 16 * lane.
-__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rsrc, void LDS_AS* lds, unsigned voff,
-                                           unsigned soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, lds, 16, voff, soff, 0, 0);
+// Issued as asm so the compiler does not order it against LDS reads of other
+// buffers (it cannot prove them disjoint and would drain the queue); every
+// wait for these loads is explicit (vmcnt) in the kernel.  The compiler's
+// hazard tracking does not look inside asm, so the leading s_nop 4 supplies
+// the wait states a buffer load needs after a VALU write of one of its SGPR
+// operands (v_readlane restoring a spilled descriptor: 5) and after the M0
+// write that sets the LDS address (1).
+__device__ __forceinline__ void load_lds16(u32x4_t rsrc, void LDS_AS* lds, unsigned voff, unsigned soff) {
+  asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+               :
+               : "v"(voff), "s"(rsrc), "s"(soff), "{m0}"((unsigned)(size_t)lds)
+               : "memory");
 }
 
 __device__ __forceinline__ unsigned pack_bf16x2(float a, float b) {
@@ -130,6 +136,29 @@ __device__ __forceinline__ float pair_sum(float x) {
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Marks x as used at this point, so its computation is not sunk past it.
+// Input-only: the producing instruction stays the last writer of the
+// registers, so the compiler still inserts the wait states its readers need.
+// (The host pass parses kernel bodies too, and its target has no such
+// register class for 64-byte operands, hence the guard.)
+template <typename T>
+__device__ __forceinline__ void keep(const T& x) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("" ::"v"(x));
+#endif
+}
+
+// Workgroup barrier without the memory fence of __syncthreads (which would
+// drain every load in flight): the caller waits for what must have landed.
+// The empty asm statements keep the compiler from moving LDS accesses across.
+__device__ __forceinline__ void wg_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // Buffer offset of the 16 bytes that belong at byte `o` of a padded LDS tile;
 // a padding slot gets an offset past any buffer end (reads as zero, touches
 // no memory).
@@ -149,7 +178,7 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ K
                      const __bf16* __restrict__ Vg, __bf16* __restrict__ Og,
                      float* __restrict__ Lg, int N, int q_tiles, float scale) {
   using T = Tile<D>;
-  // [Q tile][K buffer 0][K buffer 1][V buffer 0][V buffer 1], padded rows
+  // [K buffer 0][K buffer 1][V buffer 0][V buffer 1], padded rows
   __shared__ __attribute__((aligned(1024))) char smem[T::kLdsBytes];
 
   const int tid = threadIdx.x;
@@ -162,8 +191,8 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ K
   const int nb = gridDim.x;
   const int wg = blockIdx.x;
   const int per = nb >> 3, rem = nb & 7;
-  const int xcd = wg & 7, slot = wg >> 3;
-  const int logical = xcd * per + (xcd < rem ? xcd : rem) + slot;
+  const int xcd = wg & 7, slot_id = wg >> 3;
+  const int logical = xcd * per + (xcd < rem ? xcd : rem) + slot_id;
   const int bh = logical / q_tiles;
   const int qi = logical - bh * q_tiles;
   const int qt = CAUSAL ? (q_tiles - 1 - qi) : qi;
@@ -181,14 +210,27 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ K
   }
 
   char LDS_AS* lds = (char LDS_AS*)smem;
-  char LDS_AS* qlds = lds;
-  auto kbuf = [&](int s) { return lds + T::kQBytes + s * T::kBytes; };
-  auto vbuf = [&](int s) { return lds + T::kQBytes + (2 + s) * T::kBytes; };
+  auto kbuf = [&](int s) { return lds + s * T::kBytes; };
+  auto vbuf = [&](int s) { return lds + (2 + s) * T::kBytes; };
+
+  // ---- Q straight into registers, in the B-operand layout of S^T = K Q^T:
+  // lane (l32, g) holds Q[qrow][16 ds + 8 g + 0..7] for every d-step ds
+  // (rows past N read as zeros; their outputs are never stored)
+  bf16x8_t qf[D / 16];
+  {
+    const bf16x8_t* qp = reinterpret_cast<const bf16x8_t*>(Qg + head_off + (size_t)qrow * D) + g;
+#pragma unroll
+    for (int ds = 0; ds < D / 16; ++ds) qf[ds] = bf16x8_t{};
+    if (qrow < N) {
+#pragma unroll
+      for (int ds = 0; ds < D / 16; ++ds) qf[ds] = qp[2 * ds];
+    }
+  }
 
   // ---- buffer -> LDS loads (voffsets fixed per lane, tile offset scalar)
   const unsigned head_bytes = (unsigned)N * D * 2;
-  const __amdgpu_buffer_rsrc_t k_rsrc = make_rsrc(Kg + head_off, head_bytes);
-  const __amdgpu_buffer_rsrc_t v_rsrc = make_rsrc(Vg + head_off, head_bytes);
+  const u32x4_t k_rsrc = make_rsrc(Kg + head_off, head_bytes);
+  const u32x4_t v_rsrc = make_rsrc(Vg + head_off, head_bytes);
   unsigned k_voff[T::kLoadsPerWave], v_voff[T::kLoadsPerWave];
 #pragma unroll
   for (int p = 0; p < T::kLoadsPerWave; ++p) {
@@ -196,7 +238,7 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ K
     k_voff[p] = lds_slot_source<D>(o, false);
     v_voff[p] = lds_slot_source<D>(o, true);
   }
-  auto dma_tile = [&](__amdgpu_buffer_rsrc_t rsrc, const unsigned* voff, int tile, char LDS_AS* dst) {
+  auto dma_tile = [&](u32x4_t rsrc, const unsigned* voff, int tile, char LDS_AS* dst) {
     const unsigned soff = (unsigned)tile * kFwdBC * T::kRowBytes;
 #pragma unroll
     for (int p = 0; p < T::kLoadsPerWave; ++p) {
@@ -207,29 +249,41 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ K
   };
 
   // ---- per-lane LDS read bases (everything else is a compile-time offset)
-  // K / Q fragment (A / B operand of S^T = K Q^T): row l32, chunk 2*ds + g
-  const int kq_base = l32 * T::kStride + g * 16;
-  const int q_base = kq_base + wave * 32 * T::kStride;
+  // K fragment (A operand of S^T = K Q^T): row l32, chunk 2*ds + g
+  const int k_base = l32 * T::kStride + g * 16;
   // V^T fragment for key step ks, half t: keys ks*16 + 8t + 4g + k (k = 0..3)
   // at stored rows ks*16 + 4k + 2t + g; lanes address dims 16*((lane>>4)&1) + 4*(lane&3)
   const int v_base = (4 * ((lane & 15) >> 2) + g) * T::kStride +
                      (((lane >> 4) & 1) * 16 + (lane & 3) * 4) * 2;
-
-  // S^T tile from the K tile at `kb`: d-steps [DS0, DS1) of the contraction
-  // (DS0 == 0 starts the accumulation)
-  auto scores = [&](const char LDS_AS* kb, f32x16_t& s0, f32x16_t& s1, auto ds0_tag, auto ds1_tag) {
-    constexpr int DS0 = decltype(ds0_tag)::value, DS1 = decltype(ds1_tag)::value;
-    if constexpr (DS0 == 0) {
-      s0 = f32x16_t{};
-      s1 = f32x16_t{};
-    }
+  // A operand of U^T += V^T W^T for head-dimension block db and key step ks:
+  // two transposing reads (keys ks*16 + 8t + 4g + 0..3 for t = 0, 1)
+  auto v_frag = [&](const char LDS_AS* vb, int db, int ks) {
+    bf16x8_t a;
 #pragma unroll
-    for (int ds = DS0; ds < DS1; ++ds) {
-      const bf16x8_t qf = *(const bf16x8_t LDS_AS*)(qlds + q_base + ds * 32);
-      const bf16x8_t a0 = *(const bf16x8_t LDS_AS*)(kb + kq_base + ds * 32);
-      const bf16x8_t a1 = *(const bf16x8_t LDS_AS*)(kb + kq_base + 32 * T::kStride + ds * 32);
-      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf, s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf, s1, 0, 0, 0);
+    for (int t = 0; t < 2; ++t) {
+      const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (i16x4_t LDS_AS*)(vb + (ks * 16 + 2 * t) * T::kStride + db * 64));
+      const bf16x4_t v4 = __builtin_bit_cast(bf16x4_t, v);
+      a[4 * t + 0] = v4[0];
+      a[4 * t + 1] = v4[1];
+      a[4 * t + 2] = v4[2];
+      a[4 * t + 3] = v4[3];
+    }
+    return a;
+  };
+
+  // S^T tile (kFwdBC keys x 32 queries) from the K tile at `kb`: block c of
+  // 32 keys accumulates in s[cb]
+  auto scores = [&](const char LDS_AS* kb, f32x16_t (&s)[kKB]) {
+#pragma unroll
+    for (int cb = 0; cb < kKB; ++cb) s[cb] = f32x16_t{};
+#pragma unroll
+    for (int ds = 0; ds < D / 16; ++ds) {
+#pragma unroll
+      for (int cb = 0; cb < kKB; ++cb) {
+        const bf16x8_t a = *(const bf16x8_t LDS_AS*)(kb + k_base + cb * 32 * T::kStride + ds * 32);
+        s[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ds], s[cb], 0, 0, 0);
+      }
     }
   };
 
@@ -238,30 +292,16 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ K
     return (kbase + kFwdBC > N) || (CAUSAL && kbase + kFwdBC - 1 > qw0);
   };
   // keys past N, and keys after the query when causal, get -inf
-  auto apply_mask = [&](int j, f32x16_t& s0, f32x16_t& s1) {
+  auto apply_mask = [&](int j, f32x16_t (&s)[kKB]) {
     const int kbase = j * kFwdBC;
     const int lim = CAUSAL ? min(N - 1, qrow) : N - 1;  // last valid key
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int kr = kbase + 8 * (i >> 2) + 4 * g + (i & 3);
-      if (kr > lim) s0[i] = -INFINITY;
-      if (kr + 32 > lim) s1[i] = -INFINITY;
-    }
-  };
-
-  auto v_frag = [&](const char LDS_AS* vb, int db, int ks) {
-    bf16x8_t a;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const char LDS_AS* p = vb + v_base + (ks * 16 + 2 * t) * T::kStride + db * 64;
-      const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4_t LDS_AS*)p);
-      const bf16x4_t vb4 = __builtin_bit_cast(bf16x4_t, v);
-      a[4 * t + 0] = vb4[0];
-      a[4 * t + 1] = vb4[1];
-      a[4 * t + 2] = vb4[2];
-      a[4 * t + 3] = vb4[3];
+      for (int cb = 0; cb < kKB; ++cb)
+        if (kr + 32 * cb > lim) s[cb][i] = -INFINITY;
     }
-    return a;
   };
 
   // ---- online-softmax state: base m (raw score units, equal in lanes l and
@@ -274,43 +314,61 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ K
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) u[db] = f32x16_t{};
 
-  // ---- prologue: Q, K_0, V_0, K_1 in flight; S_0
-  {
-    const __amdgpu_buffer_rsrc_t q_rsrc = make_rsrc(Qg + head_off, head_bytes);
-    const unsigned q_soff = (unsigned)q0 * T::kRowBytes;
-#pragma unroll
-    for (int p = 0; p < T::kQLoadsPerWave; ++p) {
-      const int blk = wave + p * kFwdWaves;
-      if (blk < T::kQLoads)
-        load_lds16(q_rsrc, (void LDS_AS*)(qlds + blk * 1024),
-                   lds_slot_source<D>(blk * 1024 + lane * 16, false), q_soff);
+  // ---- slot schedule.  The loop runs in slots separated by workgroup
+  // barriers.  Each KV tile j takes two slots per wavefront: a softmax slot
+  // (VALU only: W = exp2(c S_j - c m), l, rescale) and a matrix slot (MFMA
+  // only: U^T += V_j^T W^T, then S_{j+1} = K_{j+1} Q^T).  Group 0 (waves
+  // 0-3) runs tile j in slots 2j+1, 2j+2; group 1 (waves 4-7, the other
+  // wavefront of each SIMD) one slot later, so in every slot one wavefront
+  // per SIMD keeps the matrix core busy while the other runs the softmax.
+  // Slot 0 forms S_0 everywhere; group 1 idles in slot 1.  Loads are issued
+  // in even slots 2t (t >= 1): K_{t+1} and V_t, each into the buffer whose
+  // last reader ran in slot 2t-1; they are waited for at the end of slot
+  // 2t+1, before their first reader in slot 2t+2.
+  const int grp = FA_FWD_PINGPONG ? (wave >> 2) : 0;
+  auto issue_slot = [&](int s) {
+    if ((s & 1) == 0 && s >= 2) {
+      const int t = s >> 1;
+      if (t + 1 < n_tiles) dma_tile(k_rsrc, k_voff, t + 1, kbuf((t + 1) & 1));
+      if (t < n_tiles) dma_tile(v_rsrc, v_voff, t, vbuf(t & 1));
     }
-  }
+  };
+  auto end_slot = [&](int s) {
+    if (s & 1) wait_vmem();
+    wg_barrier();
+  };
+
+  // ---- prologue: K_0, V_0, K_1 in LDS; slot 0 = S_0
   dma_tile(k_rsrc, k_voff, 0, kbuf(0));
   dma_tile(v_rsrc, v_voff, 0, vbuf(0));
   if (n_tiles > 1) dma_tile(k_rsrc, k_voff, 1, kbuf(1));
   wait_vmem();
   __syncthreads();
-  f32x16_t sc0, sc1, sn0, sn1;  // scores of two consecutive tiles
-  scores(kbuf(0), sc0, sc1, IntTag<0>{}, IntTag<D / 16>{});
-  if (needs_mask(0)) apply_mask(0, sc0, sc1);
-
-  // one KV tile: s0/s1 hold its (masked) scores; with HAS_NEXT the scores
-  // of the next tile are accumulated into n0/n1 meanwhile
-  auto step = [&](int j, f32x16_t& s0, f32x16_t& s1, f32x16_t& n0, f32x16_t& n1,
-                  auto has_next_tag) {
-    constexpr bool HAS_NEXT = decltype(has_next_tag)::value;
-    constexpr int kSplit = 2;  // d-steps of the next tile issued before the rescale branch
-    wait_vmem();
-    __syncthreads();
-    if (j + 2 < n_tiles) dma_tile(k_rsrc, k_voff, j + 2, kbuf(j & 1));
-    if (HAS_NEXT) dma_tile(v_rsrc, v_voff, j + 1, vbuf((j + 1) & 1));
-    const char LDS_AS* knext = kbuf((j + 1) & 1);
-
-    if constexpr (HAS_NEXT) scores(knext, n0, n1, IntTag<0>{}, IntTag<kSplit>{});
-    float mx = -INFINITY;
+  f32x16_t s[kKB];  // scores of the current tile
+  scores(kbuf(0), s);
+  if (needs_mask(0)) apply_mask(0, s);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) mx = fmaxf(fmaxf(mx, s0[i]), s1[i]);
+  for (int cb = 0; cb < kKB; ++cb) keep(s[cb]);
+  end_slot(0);
+  if (grp == 1) end_slot(1);  // group 1's idle slot
+
+  for (int j = 0; j < n_tiles; ++j) {
+    const int sa = 2 * j + 1 + grp;
+
+    // -- softmax slot of tile j (VALU)
+    issue_slot(sa);
+    // row max: one chain per 32-key block, then across blocks and lane pairs
+    float mxc[kKB];
+#pragma unroll
+    for (int cb = 0; cb < kKB; ++cb) {
+      float m = fmaxf(s[cb][0], s[cb][1]);
+#pragma unroll
+      for (int i = 2; i < 16; i += 2) m = fmaxf(fmaxf(m, s[cb][i]), s[cb][i + 1]);
+      mxc[cb] = m;
+    }
+    float mx = mxc[0];
+#pragma unroll
+    for (int cb = 1; cb < kKB; ++cb) mx = fmaxf(mx, mxc[cb]);
     mx = pair_max(mx);
     // move the base only if the tile max exceeds it by more than the
     // threshold (always on the first tile with a valid key)
@@ -323,72 +381,63 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ K
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) u[db] *= alpha;
     }
-
-    // softmax of tile j (VALU) overlapped with the rest of the score MFMAs
-    // of tile j+1.  The row sum adds the fp32 weights, so l (and L) carry no
-    // bf16 rounding; only the W V product sees bf16 weights.
-    if constexpr (HAS_NEXT) scores(knext, n0, n1, IntTag<kSplit>{}, IntTag<D / 16>{});
-    bf16x8_t wb[4];
-    float rs = 0.f;
+    // W in bf16 for the product, fp32 partial sums for l (so l and L carry
+    // no bf16 rounding): wb[2c + h] holds key step 2c + h
+    bf16x8_t wb[2 * kKB];
+    float rsp[2 * kKB];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      float p[8], q[8];
+    for (int cb = 0; cb < kKB; ++cb) {
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        p[t] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[8 * h + t], c, -mc));
-        q[t] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[8 * h + t], c, -mc));
-        rs += p[t] + q[t];
-      }
-      wb[h] = bf16x8_t{(__bf16)p[0], (__bf16)p[1], (__bf16)p[2], (__bf16)p[3],
-                       (__bf16)p[4], (__bf16)p[5], (__bf16)p[6], (__bf16)p[7]};
-      wb[2 + h] = bf16x8_t{(__bf16)q[0], (__bf16)q[1], (__bf16)q[2], (__bf16)q[3],
-                           (__bf16)q[4], (__bf16)q[5], (__bf16)q[6], (__bf16)q[7]};
-    }
-    l_run = alpha * l_run + rs;
-#if FA_FWD_INTERLEAVE > 0
-    if constexpr (HAS_NEXT) {
-      // one score MFMA with its fragment reads, then a run of softmax VALU
+      for (int h = 0; h < 2; ++h) {
+        float p[8];
 #pragma unroll
-      for (int i = 0; i < D / 16 - kSplit; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, FA_FWD_INTERLEAVE, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, FA_FWD_INTERLEAVE, 0);
+        for (int t = 0; t < 8; ++t) p[t] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[cb][8 * h + t], c, -mc));
+        rsp[2 * cb + h] = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+        wb[2 * cb + h] = bf16x8_t{(__bf16)p[0], (__bf16)p[1], (__bf16)p[2], (__bf16)p[3],
+                                 (__bf16)p[4], (__bf16)p[5], (__bf16)p[6], (__bf16)p[7]};
       }
     }
-#endif
+#pragma unroll
+    for (int w = 2 * kKB; w > 1; w >>= 1) {
+#pragma unroll
+      for (int i = 0; i < w / 2; ++i) rsp[i] += rsp[i + w / 2];
+    }
+    l_run = alpha * l_run + rsp[0];
+    // keep the compiler from sinking the softmax into the matrix slot
+#pragma unroll
+    for (int k = 0; k < 2 * kKB; ++k) keep(wb[k]);
+    keep(l_run);
+    end_slot(sa);
 
-    // U^T += V_j^T W^T (a wavefront with every row before this tile's first
-    // key has only zero weights here: skip it)
+    // -- matrix slot of tile j (MFMA): U^T += V_j^T W^T (a wavefront with
+    // every row before this tile's first key has only zero weights: skip
+    // it), then the scores of tile j+1
+    issue_slot(sa + 1);
     const bool wave_live = !CAUSAL || (j * kFwdBC <= qw0 + 31);
     if (wave_live) {
-      const char LDS_AS* vb = vbuf(j & 1);
+      const char LDS_AS* vb = vbuf(j & 1) + v_base;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) {
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
+        for (int ks = 0; ks < kKS; ++ks) {
           const bf16x8_t a = v_frag(vb, db, ks);
           u[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, wb[ks], u[db], 0, 0, 0);
         }
       }
     }
-    if constexpr (HAS_NEXT) {
-      if (needs_mask(j + 1)) apply_mask(j + 1, n0, n1);
+    if (j + 1 < n_tiles) {
+      scores(kbuf((j + 1) & 1), s);
+      if (needs_mask(j + 1)) apply_mask(j + 1, s);
     }
-  };
-
-  // two tiles per trip so the score registers alternate without copies
-  int j = 0;
-  for (; j + 2 < n_tiles; j += 2) {
-    step(j, sc0, sc1, sn0, sn1, BoolTag<true>{});
-    step(j + 1, sn0, sn1, sc0, sc1, BoolTag<true>{});
-  }
-  if (j + 1 < n_tiles) {
-    step(j, sc0, sc1, sn0, sn1, BoolTag<true>{});
-    step(j + 1, sn0, sn1, sc0, sc1, BoolTag<false>{});
-  } else {
-    step(j, sc0, sc1, sn0, sn1, BoolTag<false>{});
+    // keep the products in this slot
+#pragma unroll
+    for (int cb = 0; cb < kKB; ++cb) keep(s[cb]);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) keep(u[db]);
+    // every wavefront passes 2 * n_tiles + 1 barriers in the loop and slot
+    // 0: group 1 has the extra idle slot 1, so it skips the barrier after
+    // its final slot
+    if (!(grp == 1 && j == n_tiles - 1)) end_slot(sa + 1);
   }
 
   // ---- epilogue: O = U / l, L = m * scale + ln l

@@ -12,10 +12,13 @@ namespace fa {
 // KV tiles of kFwdBC keys.
 constexpr int kFwdWaves = 8;
 constexpr int kFwdBR = 32 * kFwdWaves;
-constexpr int kFwdBC = 64;
-// LDS of one prefill workgroup: the query tile and two K and two V tiles,
-// each row padded by 16 bytes.
-__host__ __device__ constexpr int fwd_lds_bytes(int d) { return (kFwdBR + 4 * kFwdBC) * (2 * d + 16); }
+#ifndef FA_FWD_BC
+#define FA_FWD_BC 64
+#endif
+constexpr int kFwdBC = FA_FWD_BC;
+// LDS of one prefill workgroup: two K and two V tiles, each row padded by 16
+// bytes (the query tile lives in registers).
+__host__ __device__ constexpr int fwd_lds_bytes(int d) { return 4 * kFwdBC * (2 * d + 16); }
 
 // fp32 prefill: one wavefront, one query row per lane, 64-key tiles.
 constexpr int kF32BR = 64;
