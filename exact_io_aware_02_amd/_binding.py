@@ -39,6 +39,7 @@ class fa_fwd_plan_t(ctypes.Structure):
         ("workgroups", ctypes.c_int64),
         ("tiles_visited", ctypes.c_int64),
         ("tiles_masked", ctypes.c_int64),
+        ("work_units", ctypes.c_int64),
     ]
 
 

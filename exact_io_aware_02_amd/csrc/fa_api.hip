@@ -89,6 +89,9 @@ int check_decode(const void* q, const void* Kc, const void* Vc, const void* o, c
   return FA_OK;
 }
 
+// Compute units assumed by the host-only planners (no device query).
+constexpr int kPlanCUs = 256;
+
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 size_t ws_bytes(int B, int H, int d, int S) {
@@ -180,7 +183,10 @@ int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* L, int B
            int d, int causal, float scale, void* stream) {
   int st = check_fwd(Q, K, V, O, L, B, H, N, d, causal, scale, 2, fa::kFwdBR);
   if (st != FA_OK) return st;
-  fa::FwdArgs a{Q, K, V, O, L, B, H, N, causal, scale};
+  int cus = 0;
+  if ((st = cu_count(&cus)) != FA_OK) return st;
+  fa::FwdArgs a{Q, K, V, O, L, B, H, N, causal, scale,
+                (int)fa::fwd_grid(fa::fwd_units(B, H, N, causal), causal, cus)};
   hipError_t e = fa::launch_fwd_bf16(a, d, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "fa_fwd launch");
   return ok();
@@ -190,7 +196,7 @@ int fa_fwd_f32(const float* Q, const float* K, const float* V, float* O, float* 
                int N, int d, int causal, float scale, void* stream) {
   int st = check_fwd(Q, K, V, O, L, B, H, N, d, causal, scale, 4, fa::kF32BR);
   if (st != FA_OK) return st;
-  fa::FwdArgs a{Q, K, V, O, L, B, H, N, causal, scale};
+  fa::FwdArgs a{Q, K, V, O, L, B, H, N, causal, scale, 0};
   hipError_t e = fa::launch_fwd_f32(a, d, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "fa_fwd_f32 launch");
   return ok();
@@ -208,7 +214,8 @@ int fa_fwd_plan(int B, int H, int N, int d, int causal, fa_fwd_plan_t* out) {
   out->kv_tiles = (int)fa::ceil_div64(N, fa::kFwdBC);
   out->threads_per_workgroup = fa::kFwdWaves * 64;
   out->lds_bytes = fa::fwd_lds_bytes(d);
-  out->workgroups = (int64_t)B * H * q_tiles;
+  out->work_units = fa::fwd_units(B, H, N, causal);
+  out->workgroups = fa::fwd_grid(out->work_units, causal, kPlanCUs);
   int64_t visited = 0, masked = 0;
   for (int qt = 0; qt < q_tiles; ++qt) {
     const int n = fa::fwd_kv_tiles_for(qt, N, causal);
@@ -235,7 +242,7 @@ int fa_decode_plan(int B, int H, int d, int num_splits, fa_decode_plan_t* out) {
   if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "head dimension %d not supported", d);
   if (num_splits < 0 || num_splits > 4096) return fail(FA_ERR_INVALID_ARG, "num_splits out of range");
   int S = num_splits;
-  if (S == 0) S = auto_splits(B, H, 256);
+  if (S == 0) S = auto_splits(B, H, kPlanCUs);
   out->num_splits = S;
   out->threads_per_workgroup = fa::kDecWaves * 64;
   out->split_workgroups = (int64_t)B * H * S;

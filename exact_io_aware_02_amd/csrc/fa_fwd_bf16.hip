@@ -176,7 +176,7 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_bf16_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ Kg,
                      const __bf16* __restrict__ Vg, __bf16* __restrict__ Og,
-                     float* __restrict__ Lg, int N, int q_tiles, float scale) {
+                     float* __restrict__ Lg, int N, int q_tiles, int units, float scale) {
   using T = Tile<D>;
   // [K buffer 0][K buffer 1][V buffer 0][V buffer 1], padded rows
   __shared__ __attribute__((aligned(1024))) char smem[T::kLdsBytes];
@@ -187,16 +187,10 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ K
   const int l32 = lane & 31;
   const int g = lane >> 5;  // lane group: which 8-wide k slice a lane feeds
 
-  // ---- workgroup -> (head, query tile): XCD-aware, longest first if causal
-  const int nb = gridDim.x;
-  const int wg = blockIdx.x;
-  const int per = nb >> 3, rem = nb & 7;
-  const int xcd = wg & 7, slot_id = wg >> 3;
-  const int logical = xcd * per + (xcd < rem ? xcd : rem) + slot_id;
-  const int bh = logical / q_tiles;
-  const int qi = logical - bh * q_tiles;
-  const int qt = CAUSAL ? (q_tiles - 1 - qi) : qi;
-
+  // One query tile (item) of head bh: Algorithm 1 over its KV tiles, then
+  // O and L.  Ends with a workgroup barrier, so the next item's loads never
+  // overwrite LDS a wavefront of this one may still read.
+  auto run_item = [&](const int bh, const int qt) {
   const size_t head_off = (size_t)bh * N * D;
   const int q0 = qt * kFwdBR;
   const int qw0 = q0 + wave * 32;  // first query row of this wavefront
@@ -460,16 +454,46 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ K
       Lg[(size_t)bh * N + qrow] = l_tot > 0.f ? m_ref * scale + __logf(l_tot) : -INFINITY;
     }
   }
+  __syncthreads();
+  };
+
+  // ---- workgroup -> work units.  A unit is one query tile, or for causal
+  // attention the pair of query tiles (p, q_tiles-1-p) of one head, so that
+  // every causal unit has the same number of KV tiles.  Causal launches are
+  // persistent: G workgroups (one per compute unit) take units logical(w),
+  // logical(w) + G, ..., a static and balanced assignment that does not
+  // depend on the order in which the hardware refills compute units.  Units
+  // are numbered head-major and the logical index places consecutive units on
+  // one XCD (dispatch is round-robin over the 8 XCDs), so the units running
+  // at once on an XCD share heads and their K/V in L2.
+  const int G = gridDim.x;
+  const int wg = blockIdx.x;
+  const int per = G >> 3, rem = G & 7;
+  const int xcd = wg & 7, slot_id = wg >> 3;
+  const int logical = xcd * per + (xcd < rem ? xcd : rem) + slot_id;
+  if constexpr (CAUSAL) {
+    const int pairs_per_head = (q_tiles + 1) >> 1;
+    for (int unit = logical; unit < units; unit += G) {
+      const int bh = unit / pairs_per_head;
+      const int p = unit - bh * pairs_per_head;
+      run_item(bh, q_tiles - 1 - p);  // the longer tile first
+      if (p < q_tiles - 1 - p) run_item(bh, p);
+    }
+  } else {
+    // one workgroup per query tile (the grid equals the unit count)
+    const int bh = logical / q_tiles;
+    run_item(bh, logical - bh * q_tiles);
+  }
 }
 
 template <int D, bool CAUSAL>
 hipError_t launch(const FwdArgs& a, hipStream_t stream) {
   const int q_tiles = (a.N + kFwdBR - 1) / kFwdBR;
-  const int64_t nb = (int64_t)a.B * a.H * q_tiles;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL>), dim3((unsigned)nb), dim3(kThreads), 0, stream,
+  const int64_t units = fwd_units(a.B, a.H, a.N, a.causal);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL>), dim3((unsigned)a.grid), dim3(kThreads), 0, stream,
                      static_cast<const __bf16*>(a.Q), static_cast<const __bf16*>(a.K),
                      static_cast<const __bf16*>(a.V), static_cast<__bf16*>(a.O), a.L, a.N, q_tiles,
-                     a.scale);
+                     (int)units, a.scale);
   return hipGetLastError();
 }
 

@@ -38,6 +38,7 @@ struct FwdArgs {
   int B, H, N;
   int causal;
   float scale;
+  int grid;  // bf16 prefill: persistent workgroups, 1 <= grid <= fwd_units
 };
 
 struct DecodeArgs {
@@ -71,6 +72,21 @@ inline int fwd_kv_tiles_for(int qt, int N, int causal) {
   if (last_row > N - 1) last_row = N - 1;
   int t = last_row / kFwdBC + 1;
   return t < kv_tiles ? t : kv_tiles;
+}
+
+// Work units of the persistent bf16 prefill grid: one query tile, or for
+// causal attention the pair of query tiles (p, q_tiles-1-p) of a head.
+inline int64_t fwd_units(int B, int H, int N, int causal) {
+  const int64_t q_tiles = ceil_div64(N, kFwdBR);
+  return (int64_t)B * H * (causal ? (q_tiles + 1) / 2 : q_tiles);
+}
+// Grid of the bf16 prefill.  Causal: persistent, one workgroup per compute
+// unit (fewer if there are fewer units), each taking every grid-th pair of
+// query tiles, so that all workgroups get the same work.  Non-causal: every
+// unit already has the same work, and one workgroup per unit lets the
+// hardware overlap one workgroup's start with another's end.
+inline int64_t fwd_grid(int64_t units, int causal, int cus) {
+  return causal ? (units < cus ? units : cus) : units;
 }
 
 // Decode chunk length for a sequence of `len` tokens split `S` ways.

@@ -58,9 +58,11 @@ typedef struct fa_fwd_plan_t {
   int kv_tiles;              /* ceil(N / B_c) per (b, h) */
   int threads_per_workgroup; /* wavefronts * 64 */
   int lds_bytes;             /* LDS per workgroup */
-  int64_t workgroups;        /* B * H * q_tiles */
+  int64_t workgroups;        /* causal: min(work_units, compute units); else work_units */
   int64_t tiles_visited;     /* (query tile, KV tile) pairs computed, all heads */
   int64_t tiles_masked;      /* of those, tiles masked on chip (diagonal/ragged) */
+  int64_t work_units;        /* B * H * q_tiles, or B * H * ceil(q_tiles / 2)
+                                causal pairs of query tiles (p, q_tiles-1-p) */
 } fa_fwd_plan_t;
 
 /* Geometry of one fa_decode launch (host-only planning; see fa_decode_plan). */
@@ -146,6 +148,10 @@ size_t fa_decode_workspace_bytes(int B, int H, int d, int num_splits);
 
 /* Host-only launch planning (no HIP call; usable without a GPU).
  * fa_fwd_plan: tile geometry and the exact number of tiles fa_fwd visits.
+ * Causal fa_fwd runs a persistent grid of one workgroup per compute unit,
+ * each taking every grid-th pair of query tiles; without a device the plan
+ * assumes 256 compute units.  Non-causal fa_fwd runs one workgroup per
+ * query tile.
  * fa_decode_plan: splits and workspace; num_splits = 0 needs the device's CU
  * count, so without a device it assumes 256 compute units.
  * fa_decode_chunk_tokens: chunk length for a sequence of kv_len tokens. */

@@ -168,7 +168,11 @@ def test_fwd_plan_tile_count_matches_oracle(N, causal):
     Q, K, V = (rng.standard_normal((N, 2)) for _ in range(3))
     _, _, cnt = oracle.tiled_ref(Q, K, V, p["block_rows"], p["block_cols"], 1.0, causal=bool(causal), count=True)
     assert p["tiles_visited"] == 6 * cnt["tiles"]
-    assert p["workgroups"] == 6 * -(-N // p["block_rows"])
+    q_tiles = -(-N // p["block_rows"])
+    assert p["q_tiles"] == q_tiles
+    # persistent grid over work units: query tiles, or causal pairs of them
+    assert p["work_units"] == 6 * (-(-q_tiles // 2) if causal else q_tiles)
+    assert p["workgroups"] == (min(p["work_units"], 256) if causal else p["work_units"])
 
 
 def test_fwd_plan_causal_pin_exercise4():
@@ -182,3 +186,21 @@ def test_fwd_plan_causal_pin_exercise4():
     T = N // p["block_rows"]
     assert p["tiles_visited"] == r * oracle.causal_tile_count(T)
     assert fa.fa_fwd_plan(1, 1, N, 128, 0)["tiles_visited"] == T * (N // p["block_cols"])
+
+
+def test_fwd_causal_pairs_balance_work():
+    """Each causal work unit pairs query tile p with q_tiles-1-p, so every
+    unit visits the same number of KV tiles (q_tiles + 1 tiles of B_r rows'
+    worth when q_tiles is even); the units cover every query tile once."""
+    fa = _fa()
+    N = 4096
+    p = fa.fa_fwd_plan(1, 1, N, 128, 1)
+    T, r = p["q_tiles"], p["block_rows"] // p["block_cols"]
+    per_tile = [r * (qt + 1) for qt in range(T)]  # KV tiles visited by query tile qt
+    units = [(q, T - 1 - q) for q in range((T + 1) // 2)]
+    covered = sorted(q for u in units for q in set(u))
+    assert covered == list(range(T))
+    work = {per_tile[a] + (per_tile[b] if b != a else 0) for a, b in units}
+    assert work == {r * (T + 1)}
+    assert p["work_units"] == len(units)
+    assert p["tiles_visited"] == sum(per_tile)
