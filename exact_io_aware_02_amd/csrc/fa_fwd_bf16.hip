@@ -187,44 +187,12 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ K
   const int l32 = lane & 31;
   const int g = lane >> 5;  // lane group: which 8-wide k slice a lane feeds
 
-  // One query tile (item) of head bh: Algorithm 1 over its KV tiles, then
-  // O and L.  Ends with a workgroup barrier, so the next item's loads never
-  // overwrite LDS a wavefront of this one may still read.
-  auto run_item = [&](const int bh, const int qt) {
-  const size_t head_off = (size_t)bh * N * D;
-  const int q0 = qt * kFwdBR;
-  const int qw0 = q0 + wave * 32;  // first query row of this wavefront
-  const int qrow = qw0 + l32;      // the query this lane's column belongs to
-
-  int n_tiles = (N + kFwdBC - 1) / kFwdBC;
-  if (CAUSAL) {
-    int last = q0 + kFwdBR - 1;
-    if (last > N - 1) last = N - 1;
-    n_tiles = min(n_tiles, last / kFwdBC + 1);
-  }
-
   char LDS_AS* lds = (char LDS_AS*)smem;
   auto kbuf = [&](int s) { return lds + s * T::kBytes; };
   auto vbuf = [&](int s) { return lds + (2 + s) * T::kBytes; };
 
-  // ---- Q straight into registers, in the B-operand layout of S^T = K Q^T:
-  // lane (l32, g) holds Q[qrow][16 ds + 8 g + 0..7] for every d-step ds
-  // (rows past N read as zeros; their outputs are never stored)
-  bf16x8_t qf[D / 16];
-  {
-    const bf16x8_t* qp = reinterpret_cast<const bf16x8_t*>(Qg + head_off + (size_t)qrow * D) + g;
-#pragma unroll
-    for (int ds = 0; ds < D / 16; ++ds) qf[ds] = bf16x8_t{};
-    if (qrow < N) {
-#pragma unroll
-      for (int ds = 0; ds < D / 16; ++ds) qf[ds] = qp[2 * ds];
-    }
-  }
-
-  // ---- buffer -> LDS loads (voffsets fixed per lane, tile offset scalar)
-  const unsigned head_bytes = (unsigned)N * D * 2;
-  const u32x4_t k_rsrc = make_rsrc(Kg + head_off, head_bytes);
-  const u32x4_t v_rsrc = make_rsrc(Vg + head_off, head_bytes);
+  // ---- buffer -> LDS loads: per-lane offsets within a tile (the tile
+  // offset is scalar)
   unsigned k_voff[T::kLoadsPerWave], v_voff[T::kLoadsPerWave];
 #pragma unroll
   for (int p = 0; p < T::kLoadsPerWave; ++p) {
@@ -232,7 +200,7 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ K
     k_voff[p] = lds_slot_source<D>(o, false);
     v_voff[p] = lds_slot_source<D>(o, true);
   }
-  auto dma_tile = [&](u32x4_t rsrc, const unsigned* voff, int tile, char LDS_AS* dst) {
+  auto dma_tile = [&](const u32x4_t rsrc, const unsigned* voff, int tile, char LDS_AS* dst) {
     const unsigned soff = (unsigned)tile * kFwdBC * T::kRowBytes;
 #pragma unroll
     for (int p = 0; p < T::kLoadsPerWave; ++p) {
@@ -241,6 +209,7 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ K
         load_lds16(rsrc, (void LDS_AS*)(dst + blk * 1024), voff[p], soff);
     }
   };
+  const unsigned head_bytes = (unsigned)N * D * 2;
 
   // ---- per-lane LDS read bases (everything else is a compile-time offset)
   // K fragment (A operand of S^T = K Q^T): row l32, chunk 2*ds + g
@@ -265,6 +234,59 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ K
     }
     return a;
   };
+
+  const float c = scale * kLog2e;
+  const float theta = kRescaleLog2 / c;  // threshold in raw score units
+  const int grp = FA_FWD_PINGPONG ? (wave >> 2) : 0;
+
+  // ---- per-item state: Q fragments (B-operand layout of S^T = K Q^T: lane
+  // (l32, g) holds Q[qrow][16 ds + 8 g + 0..7] for every d-step ds), the
+  // online-softmax base m (raw score units, equal in lanes l and l^32), the
+  // per-lane partial l over the lane's keys, and the U^T accumulators
+  bf16x8_t qf[D / 16];
+  float m_ref, l_run;
+  f32x16_t u[D / 32];
+
+  // KV tiles of query tile qt (causal tiles wholly in the future skipped)
+  auto tiles_of = [&](int qt) {
+    int n = (N + kFwdBC - 1) / kFwdBC;
+    if (CAUSAL) {
+      int last = qt * kFwdBR + kFwdBR - 1;
+      if (last > N - 1) last = N - 1;
+      n = min(n, last / kFwdBC + 1);
+    }
+    return n;
+  };
+
+  // ---- start of an item (query tile qt of head bh): Q into registers and
+  // K_0, V_0, K_1 into LDS.  Only issues loads; the item waits for them.
+  auto start_item = [&](const int bh, const int qt) {
+    const size_t head_off = (size_t)bh * N * D;
+    const int qrow = qt * kFwdBR + wave * 32 + l32;
+    // rows past N read as zeros; their outputs are never stored
+    const bf16x8_t* qp = reinterpret_cast<const bf16x8_t*>(Qg + head_off + (size_t)qrow * D) + g;
+#pragma unroll
+    for (int ds = 0; ds < D / 16; ++ds) qf[ds] = bf16x8_t{};
+    if (qrow < N) {
+#pragma unroll
+      for (int ds = 0; ds < D / 16; ++ds) qf[ds] = qp[2 * ds];
+    }
+    const u32x4_t k_rsrc = make_rsrc(Kg + head_off, head_bytes);
+    const u32x4_t v_rsrc = make_rsrc(Vg + head_off, head_bytes);
+    dma_tile(k_rsrc, k_voff, 0, kbuf(0));
+    dma_tile(v_rsrc, v_voff, 0, vbuf(0));
+    if (tiles_of(qt) > 1) dma_tile(k_rsrc, k_voff, 1, kbuf(1));
+  };
+
+  // ---- one item: Algorithm 1 over its KV tiles, leaving (m, l, U).  Ends
+  // with a workgroup barrier after which no wavefront reads this item's LDS.
+  auto run_item = [&](const int bh, const int qt) {
+  const size_t head_off = (size_t)bh * N * D;
+  const int qw0 = qt * kFwdBR + wave * 32;  // first query row of this wavefront
+  const int qrow = qw0 + l32;               // the query this lane's column belongs to
+  const int n_tiles = tiles_of(qt);
+  const u32x4_t k_rsrc = make_rsrc(Kg + head_off, head_bytes);
+  const u32x4_t v_rsrc = make_rsrc(Vg + head_off, head_bytes);
 
   // S^T tile (kFwdBC keys x 32 queries) from the K tile at `kb`: block c of
   // 32 keys accumulates in s[cb]
@@ -298,13 +320,8 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ K
     }
   };
 
-  // ---- online-softmax state: base m (raw score units, equal in lanes l and
-  // l^32), per-lane partial l over the lane's keys, and U^T accumulators.
-  const float c = scale * kLog2e;
-  const float theta = kRescaleLog2 / c;  // threshold in raw score units
-  float m_ref = -INFINITY;
-  float l_run = 0.f;
-  f32x16_t u[D / 32];
+  m_ref = -INFINITY;
+  l_run = 0.f;
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) u[db] = f32x16_t{};
 
@@ -319,7 +336,6 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ K
   // in even slots 2t (t >= 1): K_{t+1} and V_t, each into the buffer whose
   // last reader ran in slot 2t-1; they are waited for at the end of slot
   // 2t+1, before their first reader in slot 2t+2.
-  const int grp = FA_FWD_PINGPONG ? (wave >> 2) : 0;
   auto issue_slot = [&](int s) {
     if ((s & 1) == 0 && s >= 2) {
       const int t = s >> 1;
@@ -332,10 +348,8 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ K
     wg_barrier();
   };
 
-  // ---- prologue: K_0, V_0, K_1 in LDS; slot 0 = S_0
-  dma_tile(k_rsrc, k_voff, 0, kbuf(0));
-  dma_tile(v_rsrc, v_voff, 0, vbuf(0));
-  if (n_tiles > 1) dma_tile(k_rsrc, k_voff, 1, kbuf(1));
+  // ---- slot 0: the loads of start_item have landed (and the stores of the
+  // previous item's O are complete), S_0 everywhere
   wait_vmem();
   __syncthreads();
   f32x16_t s[kKB];  // scores of the current tile
@@ -434,7 +448,15 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ K
     if (!(grp == 1 && j == n_tiles - 1)) end_slot(sa + 1);
   }
 
-  // ---- epilogue: O = U / l, L = m * scale + ln l
+  // every wavefront has finished reading this item's K/V tiles
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  wg_barrier();
+  };
+
+  // ---- end of an item: O = U / l, L = m * scale + ln l
+  auto finish_item = [&](const int bh, const int qt) {
+  const size_t head_off = (size_t)bh * N * D;
+  const int qrow = qt * kFwdBR + wave * 32 + l32;
   const float l_tot = pair_sum(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (qrow < N) {
@@ -454,7 +476,6 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ K
       Lg[(size_t)bh * N + qrow] = l_tot > 0.f ? m_ref * scale + __logf(l_tot) : -INFINITY;
     }
   }
-  __syncthreads();
   };
 
   // ---- workgroup -> work units.  A unit is one query tile, or for causal
@@ -472,17 +493,47 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ K
   const int xcd = wg & 7, slot_id = wg >> 3;
   const int logical = xcd * per + (xcd < rem ? xcd : rem) + slot_id;
   if constexpr (CAUSAL) {
+    // items in order: per unit the longer query tile, then the shorter one;
+    // the next item's loads are issued before this item's O is stored
     const int pairs_per_head = (q_tiles + 1) >> 1;
-    for (int unit = logical; unit < units; unit += G) {
-      const int bh = unit / pairs_per_head;
-      const int p = unit - bh * pairs_per_head;
-      run_item(bh, q_tiles - 1 - p);  // the longer tile first
-      if (p < q_tiles - 1 - p) run_item(bh, p);
+    int unit = logical, second = 0;
+    auto item_of = [&](int un, int sec, int& bh, int& qt) {
+      bh = un / pairs_per_head;
+      const int p = un - bh * pairs_per_head;
+      qt = sec ? p : q_tiles - 1 - p;
+    };
+    int bh, qt;
+    item_of(unit, second, bh, qt);
+    start_item(bh, qt);
+    for (;;) {
+      run_item(bh, qt);
+      // advance: the shorter tile of this pair if it is distinct, else the
+      // next unit
+      const int p = unit - (unit / pairs_per_head) * pairs_per_head;
+      if (second == 0 && p < q_tiles - 1 - p) {
+        second = 1;
+      } else {
+        second = 0;
+        unit += G;
+      }
+      const bool more = unit < units;
+      int nbh = 0, nqt = 0;
+      if (more) {
+        item_of(unit, second, nbh, nqt);
+        start_item(nbh, nqt);
+      }
+      finish_item(bh, qt);
+      if (!more) break;
+      bh = nbh;
+      qt = nqt;
     }
   } else {
     // one workgroup per query tile (the grid equals the unit count)
     const int bh = logical / q_tiles;
-    run_item(bh, logical - bh * q_tiles);
+    const int qt = logical - bh * q_tiles;
+    start_item(bh, qt);
+    run_item(bh, qt);
+    finish_item(bh, qt);
   }
 }
 
