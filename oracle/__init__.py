@@ -18,8 +18,8 @@ Sources (three web pages on one subject; cited by title and section):
   sequence partitioning, per-chunk partials, log-sum-exp reduction).
 * "CMU 10-423 Lecture 18: FlashAttention & efficient decoding" notes,
   sections 2.1-2.3 (online softmax, (m, l, o) merging), 3.2-3.4 (tiled forward,
-  FA-2 loop order), 4.1 and 4.3 (IO counts, causal tile skipping) and
-  Exercises 1-4.
+  FA-2 loop order), 4.1 and 4.3 (IO counts, causal tile skipping), 7.3 (KV
+  cache in blocks behind a block table) and Exercises 1-4.
 
 Modules:
 
@@ -29,6 +29,9 @@ Modules:
   merge, and the Flash-Decoding combine of (O^(k), m^(k), l^(k)) partials.
 * ``tiled``      -- Algorithm 1 of "Infra: Flash Attention" taken step by step
   with tile counters, and the closed-form IO counts of the lecture notes.
+* ``paged``      -- decode against a KV cache kept in fixed-size blocks and
+  read through a block table (lecture notes, section 7.3), both as the plain
+  definition on the gathered cache and block by block with (m, l, u) merges.
 
 Parity status: every function here is pinned by a CPU test under ``tests/``
 (values printed on the pages, closed forms, a library routine, or brute force).
@@ -45,6 +48,7 @@ from .online import (
     per_block_softmax,
 )
 from .tiled import tiled_ref, io_standard, io_fa2, io_fa1_main, causal_tile_count
+from .paged import blocks_of, gather_paged, decode_paged_ref, decode_paged_blockwise
 
 __all__ = [
     "attention_ref",
@@ -61,4 +65,8 @@ __all__ = [
     "io_fa2",
     "io_fa1_main",
     "causal_tile_count",
+    "blocks_of",
+    "gather_paged",
+    "decode_paged_ref",
+    "decode_paged_blockwise",
 ]

@@ -16,6 +16,10 @@ section 4):
   causal_4k      B=4 H=32 N=4096 d=128 bf16 N(0,1), causal
   decode_32k     B=1 H=32 L=32768 d=128 bf16 N(0,1)
   decode_varlen  B=8 H=32 d=128, L_b uniform on [4096, 65536], bf16 2*N(0,1)
+  decode_paged   decode_varlen's shapes and lengths with the cache in blocks
+                 of 16 tokens at seeded, scattered physical positions behind a
+                 block table (the layout of "CMU 10-423 Lecture 18", section
+                 7.3), bf16 2*N(0,1)
 """
 
 import numpy as np
@@ -26,6 +30,8 @@ WORKLOADS = {
     "causal_4k": dict(kind="prefill", B=4, H=32, N=4096, d=128, dtype="bf16", causal=True, vscale=1.0, seed=3),
     "decode_32k": dict(kind="decode", B=1, H=32, L=32768, d=128, dtype="bf16", vscale=1.0, seed=4),
     "decode_varlen": dict(kind="decode", B=8, H=32, Lmin=4096, Lmax=65536, d=128, dtype="bf16", vscale=2.0, seed=5),
+    "decode_paged": dict(kind="paged", B=8, H=32, Lmin=4096, Lmax=65536, d=128, dtype="bf16", vscale=2.0, seed=6,
+                         block_size=16, spare_blocks=64),
 }
 
 
@@ -100,3 +106,45 @@ def packed_offsets(lengths, H, d):
     """Element offset of sequence b's [H, L_b, d] block in a packed cache."""
     lengths = np.asarray(lengths, dtype=np.int64)
     return np.concatenate([[0], np.cumsum(lengths)[:-1]]) * H * d
+
+
+def block_table(lengths, block_size, spare_blocks=0, seed=0):
+    """A seeded block table: (table int32 [B, max_blocks], num_blocks).
+
+    Every physical block id in [0, num_blocks) is dealt once, in the order of
+    a seeded permutation, to the sequences' logical blocks (sequence 0 first);
+    `spare_blocks` ids stay unused, and entries past a sequence's blocks are
+    -1."""
+    lengths = np.asarray(lengths, dtype=np.int64)
+    nbs = [-(-int(L) // int(block_size)) for L in lengths]
+    num_blocks = sum(nbs) + int(spare_blocks)
+    perm = np.random.default_rng(seed).permutation(num_blocks)
+    table = np.full((len(lengths), max(1, max(nbs) if nbs else 1)), -1, dtype=np.int32)
+    k = 0
+    for b, n in enumerate(nbs):
+        table[b, :n] = perm[k:k + n]
+        k += n
+    return table, num_blocks
+
+
+def paged_inputs(name_or_cfg, device, lengths=None, block_size=None, spare_blocks=None, seed_offset=0):
+    """(q [B,H,d], Kpool, Vpool [num_blocks, H, block_size, d], table int32
+    [B, max_blocks], lengths) for a paged decode workload.  Pool slots that
+    hold no token are filled with draws too (never read by a correct
+    reader)."""
+    cfg = WORKLOADS[name_or_cfg] if isinstance(name_or_cfg, str) else name_or_cfg
+    B, H, d = cfg["B"], cfg["H"], cfg["d"]
+    bs = int(block_size if block_size is not None else cfg["block_size"])
+    spare = int(spare_blocks if spare_blocks is not None else cfg.get("spare_blocks", 0))
+    if lengths is None:
+        if "L" in cfg:
+            lengths = np.full((B,), cfg["L"], dtype=np.int64)
+        else:
+            lengths = varlen_lengths(B, cfg["Lmin"], cfg["Lmax"])
+    lengths = np.asarray(lengths, dtype=np.int64)
+    base = 1000 * (cfg["seed"] + seed_offset)
+    table, num_blocks = block_table(lengths, bs, spare, seed=base + 3)
+    q = torch_normal(base + 0, (B, H, d), device, cfg["dtype"], cfg["vscale"])
+    Kp = torch_normal(base + 1, (num_blocks, H, bs, d), device, cfg["dtype"], cfg["vscale"])
+    Vp = torch_normal(base + 2, (num_blocks, H, bs, d), device, cfg["dtype"], cfg["vscale"])
+    return q, Kp, Vp, table, lengths

@@ -141,3 +141,44 @@ def test_tiled_visiting_future_tiles_is_caught(monkeypatch):
 def test_io_formula_off_by_one_term_is_caught(monkeypatch):
     monkeypatch.setattr(oracle, "io_fa2", lambda N, d, Br: 2 * N * d * (-(-N // Br)) + 2 * N * d)
     assert _fails(pins.test_io_counts_exercise3)
+
+
+# ---- paged-KV decode oracle ("CMU 10-423 Lecture 18", section 7.3)
+
+import oracle.paged as pgd
+import tests.test_oracle_paged as ppins
+
+
+def test_gather_ignoring_the_block_table_is_caught(monkeypatch):
+    def logical_gather(pool, table_row, length, block_size):
+        nb = pgd.blocks_of(length, block_size)
+        H, d = pool.shape[1], pool.shape[3]
+        if nb == 0:
+            return np.zeros((H, 0, d))
+        parts = [np.asarray(pool[i], dtype=np.float64) for i in range(nb)]  # logical index, no table
+        return np.concatenate(parts, axis=1)[:, :length]
+
+    monkeypatch.setattr(pgd, "gather_paged", logical_gather)
+    monkeypatch.setattr(oracle, "gather_paged", logical_gather)
+    assert _fails(ppins.test_worked_example_section73)
+    assert _fails(ppins.test_gather_is_exact_and_blockwise_matches_plain, 4, 17)
+
+
+def test_reading_the_whole_last_block_is_caught(monkeypatch):
+    def untrimmed(pool, table_row, length, block_size):
+        nb = pgd.blocks_of(length, block_size)
+        H, d = pool.shape[1], pool.shape[3]
+        if nb == 0:
+            return np.zeros((H, 0, d))
+        return np.concatenate([np.asarray(pool[int(table_row[i])], dtype=np.float64) for i in range(nb)], axis=1)
+
+    monkeypatch.setattr(pgd, "gather_paged", untrimmed)
+    assert _fails(ppins.test_slots_past_the_end_are_never_read)
+
+
+def test_blockwise_without_rescaling_is_caught(monkeypatch):
+    def naive_merge(a, b):  # adds states without moving them to a common base
+        return (max(a[0], b[0]), a[1] + b[1], np.asarray(a[2], dtype=np.float64) + np.asarray(b[2], dtype=np.float64))
+
+    monkeypatch.setattr(pgd, "merge", naive_merge)
+    assert _fails(ppins.test_worked_example_section73)
