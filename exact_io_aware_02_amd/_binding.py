@@ -67,6 +67,8 @@ def _load():
         "fa_decode": (I, [P, P, P, P, I, I, P, I, I, P]),
         "fa_decode_ex": (I, [P, P, P, P, P, I, I, P, I, I, I, F, P, Z, P]),
         "fa_decode_workspace_bytes": (Z, [I, I, I, I]),
+        "fa_decode_paged": (I, [P, P, P, P, P, I, I, P, I, P, I, I, I, I, F, P, Z, P]),
+        "fa_decode_paged_splits": (I, [I, I, I, I, I]),
         "fa_fwd_plan": (I, [I, I, I, I, I, ctypes.POINTER(fa_fwd_plan_t)]),
         "fa_decode_plan": (I, [I, I, I, I, ctypes.POINTER(fa_decode_plan_t)]),
         "fa_decode_chunk_tokens": (I, [I, I]),
@@ -91,6 +93,8 @@ EXPORTED = (
     "fa_decode",
     "fa_decode_ex",
     "fa_decode_workspace_bytes",
+    "fa_decode_paged",
+    "fa_decode_paged_splits",
     "fa_fwd_plan",
     "fa_decode_plan",
     "fa_decode_chunk_tokens",
@@ -242,4 +246,43 @@ def fa_decode_ex(q, Kcache, Vcache, o, Lkv, workspace, lse_out=None, kv_seq_capa
     _check(lib.fa_decode_ex(_ptr(q), _ptr(Kcache), _ptr(Vcache), _ptr(o), _ptr(lse_out), B, H,
                             _ptr(Lkv), int(kv_seq_capacity), d, int(num_splits), float(scale),
                             _ptr(workspace), nbytes, _stream_ptr(stream)))
+    return o, lse_out
+
+
+def fa_decode_paged_splits(B, H, max_blocks, block_size, num_splits=0):
+    """Split count fa_decode_paged uses (0 if the arguments are invalid)."""
+    return lib.fa_decode_paged_splits(int(B), int(H), int(max_blocks), int(block_size), int(num_splits))
+
+
+def fa_decode_paged(q, Kpool, Vpool, o, block_table, Lkv, lse_out=None, num_splits=0, scale=None,
+                    workspace=None, stream=None):
+    """Flash-Decoding through a block table: q, o bf16 [B, H, d]; Kpool/Vpool
+    bf16 [num_blocks, H, block_size, d]; block_table int32 [B, max_blocks];
+    Lkv int32 [B]; optional lse_out fp32 [B, H]; workspace a device tensor
+    (None = the library's own)."""
+    import torch
+
+    B, H, d = q.shape
+    _expect(q, torch.bfloat16, (B, H, d), "q")
+    _expect(o, torch.bfloat16, (B, H, d), "o")
+    _expect(Lkv, torch.int32, (B,), "Lkv")
+    if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] != B \
+            or not block_table.is_contiguous() or block_table.device.type != "cuda":
+        raise ValueError("block_table must be a contiguous int32 device tensor [B, max_blocks]")
+    for t_, n in ((Kpool, "Kpool"), (Vpool, "Vpool")):
+        if t_.dtype != torch.bfloat16 or t_.dim() != 4 or not t_.is_contiguous() or t_.device.type != "cuda" \
+                or t_.shape[1] != H or t_.shape[3] != d:
+            raise ValueError(f"{n} must be a contiguous bf16 device tensor [num_blocks, H, block_size, d]")
+    if Kpool.shape != Vpool.shape:
+        raise ValueError("Kpool and Vpool must have the same shape")
+    num_blocks, _, block_size, _ = Kpool.shape
+    if lse_out is not None:
+        _expect(lse_out, torch.float32, (B, H), "lse_out")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.fa_decode_paged(_ptr(q), _ptr(Kpool), _ptr(Vpool), _ptr(o), _ptr(lse_out), B, H,
+                               _ptr(block_table), int(block_table.shape[1]), _ptr(Lkv), int(num_blocks),
+                               int(block_size), d, int(num_splits), float(scale), _ptr(workspace), nbytes,
+                               _stream_ptr(stream)))
     return o, lse_out

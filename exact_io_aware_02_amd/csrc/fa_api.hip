@@ -137,8 +137,14 @@ struct Workspace {
 std::mutex g_ws_mu;
 std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
 
+struct PagedArgs {
+  const int32_t* table = nullptr;
+  int max_blocks = 0, log2_bs = 0, num_blocks = 0;
+};
+
 int decode_common(const void* q, const void* Kc, const void* Vc, void* o, float* lse, int B, int H,
-                  const int32_t* Lkv, int cap, int d, int S, float scale, void* ws, hipStream_t st) {
+                  const int32_t* Lkv, int cap, int d, int S, float scale, void* ws, hipStream_t st,
+                  const PagedArgs& pg = PagedArgs()) {
   fa::DecodeArgs a;
   a.q = q;
   a.K = Kc;
@@ -154,9 +160,47 @@ int decode_common(const void* q, const void* Kc, const void* Vc, void* o, float*
   a.S = S;
   a.capacity = cap;
   a.scale = scale;
+  a.table = pg.table;
+  a.max_blocks = pg.max_blocks;
+  a.log2_bs = pg.log2_bs;
+  a.num_blocks = pg.num_blocks;
   hipError_t e = fa::launch_decode(a, d, st);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   return ok();
+}
+
+// The library-owned decode workspace of (current device, stream), grown to
+// at least `need` bytes (never while the stream is being captured).
+int internal_workspace(size_t need, hipStream_t hs, void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  std::lock_guard<std::mutex> lk(g_ws_mu);
+  Workspace& w = g_ws[std::make_pair(dev, hs)];
+  if (w.bytes < need) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    e = hipStreamIsCapturing(hs, &cs);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamIsCapturing");
+    if (cs != hipStreamCaptureStatusNone)
+      return fail(FA_ERR_WORKSPACE, "the decode workspace must grow to %zu bytes; call once outside stream capture", need);
+    if (w.ptr) {
+      e = hipStreamSynchronize(hs);
+      if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+      e = hipFree(w.ptr);
+      w.ptr = nullptr;
+      w.bytes = 0;
+      if (e != hipSuccess) return hip_fail(e, "hipFree");
+    }
+    e = hipMalloc(&w.ptr, need);
+    if (e != hipSuccess) {
+      w.ptr = nullptr;
+      (void)hipGetLastError();
+      return fail(FA_ERR_NOMEM, "hipMalloc(%zu) for the decode workspace failed", need);
+    }
+    w.bytes = need;
+  }
+  *out = w.ptr;
+  return FA_OK;
 }
 
 }  // namespace
@@ -275,37 +319,8 @@ int fa_decode(const void* q, const void* Kcache, const void* Vcache, void* o, in
   }
   const size_t need = ws_bytes(B, H, d, S);
   hipStream_t hs = static_cast<hipStream_t>(stream);
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
   void* ws = nullptr;
-  {
-    std::lock_guard<std::mutex> lk(g_ws_mu);
-    Workspace& w = g_ws[std::make_pair(dev, hs)];
-    if (w.bytes < need) {
-      hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-      e = hipStreamIsCapturing(hs, &cs);
-      if (e != hipSuccess) return hip_fail(e, "hipStreamIsCapturing");
-      if (cs != hipStreamCaptureStatusNone)
-        return fail(FA_ERR_WORKSPACE, "fa_decode workspace must grow to %zu bytes; call once outside stream capture", need);
-      if (w.ptr) {
-        e = hipStreamSynchronize(hs);
-        if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
-        e = hipFree(w.ptr);
-        w.ptr = nullptr;
-        w.bytes = 0;
-        if (e != hipSuccess) return hip_fail(e, "hipFree");
-      }
-      e = hipMalloc(&w.ptr, need);
-      if (e != hipSuccess) {
-        w.ptr = nullptr;
-        (void)hipGetLastError();
-        return fail(FA_ERR_NOMEM, "hipMalloc(%zu) for the decode workspace failed", need);
-      }
-      w.bytes = need;
-    }
-    ws = w.ptr;
-  }
+  if ((st = internal_workspace(need, hs, &ws)) != FA_OK) return st;
   return decode_common(q, Kcache, Vcache, o, nullptr, B, H, Lkv, 0, d, S, scale, ws, hs);
 }
 
@@ -329,6 +344,78 @@ int fa_decode_ex(const void* q, const void* Kcache, const void* Vcache, void* o,
     return fail(FA_ERR_INVALID_ARG, "workspace overlaps q or o");
   return decode_common(q, Kcache, Vcache, o, lse_out, B, H, Lkv, kv_seq_capacity, d, S, scale,
                        workspace, static_cast<hipStream_t>(stream));
+}
+
+int fa_decode_paged(const void* q, const void* Kpool, const void* Vpool, void* o, float* lse_out,
+                    int B, int H, const int32_t* block_table, int max_blocks, const int32_t* Lkv,
+                    int num_blocks, int block_size, int d, int num_splits, float scale,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_decode(q, Kpool, Vpool, o, lse_out, B, H, Lkv, 0, d, num_splits, scale);
+  if (st != FA_OK) return st;
+  if (!block_table) return fail(FA_ERR_INVALID_ARG, "null pointer argument (block_table)");
+  if (!aligned(block_table, 4)) return fail(FA_ERR_INVALID_ARG, "block_table misaligned");
+  if (max_blocks < 1 || num_blocks < 1)
+    return fail(FA_ERR_INVALID_ARG, "max_blocks and num_blocks must be >= 1 (got %d, %d)", max_blocks, num_blocks);
+  if (block_size < fa::kPagedMinBlock || block_size > fa::kPagedMaxBlock || (block_size & (block_size - 1)))
+    return fail(FA_ERR_INVALID_ARG, "block_size must be a power of two in [%d, %d] (got %d)", fa::kPagedMinBlock,
+                fa::kPagedMaxBlock, block_size);
+  const int64_t pool_rows = (int64_t)num_blocks * H * block_size;
+  if (pool_rows > ((int64_t)1 << 40)) return fail(FA_ERR_INVALID_ARG, "pool too large");
+  const size_t ob = (size_t)B * H * d * 2, tb = (size_t)B * max_blocks * 4;
+  if (overlap(o, ob, block_table, tb) || (lse_out && overlap(lse_out, (size_t)B * H * 4, block_table, tb)))
+    return fail(FA_ERR_INVALID_ARG, "an output overlaps block_table");
+  // split count: each chunk may span at most kPagedIdsPerChunk blocks
+  int64_t max_len = (int64_t)max_blocks * block_size;
+  if (max_len > 0x7fffffff) max_len = 0x7fffffff;
+  auto blocks_ok = [&](int S) {
+    return fa::paged_blocks_per_chunk(fa::decode_chunk_tokens((int)max_len, S), block_size) <= fa::kPagedIdsPerChunk;
+  };
+  int S = num_splits;
+  if (S == 0) {
+    int cus = 0;
+    if ((st = cu_count(&cus)) != FA_OK) return st;
+    S = auto_splits(B, H, cus);
+    while (!blocks_ok(S) && S < 4096) S = S * 2 > 4096 ? 4096 : S * 2;
+  }
+  if (!blocks_ok(S))
+    return fail(FA_ERR_UNSUPPORTED, "with %d splits a chunk may span more than %d blocks; use more splits", S,
+                fa::kPagedIdsPerChunk);
+  const size_t need = ws_bytes(B, H, d, S);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  void* ws = workspace;
+  if (!workspace) {
+    if (workspace_bytes != 0) return fail(FA_ERR_WORKSPACE, "null workspace with nonzero workspace_bytes");
+    if ((st = internal_workspace(need, hs, &ws)) != FA_OK) return st;
+  } else {
+    if (!aligned(workspace, 256)) return fail(FA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    if (workspace_bytes < need)
+      return fail(FA_ERR_WORKSPACE, "workspace of %zu bytes is too small (%zu needed)", workspace_bytes, need);
+    if (overlap(workspace, need, o, ob) || overlap(workspace, need, q, ob) || overlap(workspace, need, block_table, tb))
+      return fail(FA_ERR_INVALID_ARG, "workspace overlaps another buffer");
+  }
+  PagedArgs pg;
+  pg.table = block_table;
+  pg.max_blocks = max_blocks;
+  pg.log2_bs = 31 - __builtin_clz((unsigned)block_size);
+  pg.num_blocks = num_blocks;
+  return decode_common(q, Kpool, Vpool, o, lse_out, B, H, Lkv, 0, d, S, scale, ws, hs, pg);
+}
+
+int fa_decode_paged_splits(int B, int H, int max_blocks, int block_size, int num_splits) {
+  if (B < 1 || H < 1 || max_blocks < 1 || num_splits < 0 || num_splits > 4096) return 0;
+  if (block_size < fa::kPagedMinBlock || block_size > fa::kPagedMaxBlock || (block_size & (block_size - 1))) return 0;
+  int64_t max_len = (int64_t)max_blocks * block_size;
+  if (max_len > 0x7fffffff) max_len = 0x7fffffff;
+  int S = num_splits;
+  if (S == 0) {
+    int cus = 0;
+    if (cu_count(&cus) != FA_OK) cus = kPlanCUs;
+    S = auto_splits(B, H, cus);
+    while (fa::paged_blocks_per_chunk(fa::decode_chunk_tokens((int)max_len, S), block_size) > fa::kPagedIdsPerChunk &&
+           S < 4096)
+      S = S * 2 > 4096 ? 4096 : S * 2;
+  }
+  return fa::paged_blocks_per_chunk(fa::decode_chunk_tokens((int)max_len, S), block_size) <= fa::kPagedIdsPerChunk ? S : 0;
 }
 
 int fa_release_workspace(void) {

@@ -24,6 +24,16 @@
 //    An empty chunk writes (0, -inf).
 // Combine kernel, grid (H, B): M = max_k lse_k, w_k = e^{lse_k - M},
 // o = sum_k w_k O^(k) / sum_k w_k, lse = M + ln sum_k w_k.
+//
+// Paged caches ("CMU 10-423 Lecture 18" notes, section 7.3): the cache is a
+// pool of blocks of 2^log2_bs tokens, [num_blocks, H, block_size, d], and a
+// block table maps each sequence's logical block to a physical one.  The
+// split kernel stages its chunk's physical block ids in LDS once; every row
+// address is then pool + ((id * H + h) * block_size + key % block_size) * d.
+// block_size >= 16 keeps the rows of one load instruction inside one block.
+// Ids outside [0, num_blocks) are never dereferenced: their tokens are
+// skipped as if masked.  Per-chunk partials and the combine are the same as
+// for a contiguous cache, so identical keys give identical results.
 
 #include "fa_internal.h"
 
@@ -61,11 +71,12 @@ __device__ __forceinline__ void bf16x8_to_f32(const u32x4_t v, float* f) {
   }
 }
 
-template <int D>
+template <int D, bool PAGED>
 __global__ __launch_bounds__(kThreads) void decode_split_kernel(
     const __bf16* __restrict__ qg, const __bf16* __restrict__ Kg, const __bf16* __restrict__ Vg,
     const int32_t* __restrict__ Lkv, float* __restrict__ part_o, float* __restrict__ part_lse,
-    int H, int S, int capacity, float scale) {
+    int H, int S, int capacity, float scale, const int32_t* __restrict__ table, int max_blocks,
+    int log2_bs, int num_blocks) {
   constexpr int CPR = D / 8;        // lanes per key row (16-byte chunks per row)
   constexpr int KPI = 64 / CPR;     // key rows per wavefront load instruction
   constexpr int KPB = KPI * kUnroll;  // keys per wavefront block
@@ -73,6 +84,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
   __shared__ long long red64[kThreads];
   __shared__ float wstate[kDecWaves][2];
   __shared__ __attribute__((aligned(16))) float wacc[kDecWaves][D];
+  __shared__ int ids[PAGED ? kPagedIdsPerChunk : 1];
 
   const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -82,8 +94,11 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
   // sequence length and the start of (b, h) in the cache
   int len = Lkv[b];
   len = len < 0 ? 0 : len;
-  size_t row0;
-  if (capacity > 0) {
+  size_t row0 = 0;
+  if (PAGED) {
+    const long long cap = (long long)max_blocks << log2_bs;
+    len = len > cap ? (int)cap : len;
+  } else if (capacity > 0) {
     len = len > capacity ? capacity : len;
     row0 = ((size_t)b * H + h) * (size_t)capacity;
   } else {
@@ -126,6 +141,14 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
   const __bf16* Kh = Kg + row0 * D;
   const __bf16* Vh = Vg + row0 * D;
 
+  // paged: this chunk's physical block ids (the host bounds their count)
+  const int e_first = start >> log2_bs;
+  if (PAGED) {
+    const int e_last = (end - 1) >> log2_bs;
+    for (int e = e_first + tid; e <= e_last; e += kThreads) ids[e - e_first] = table[(size_t)b * max_blocks + e];
+    __syncthreads();
+  }
+
   float m = -INFINITY, l = 0.f;
   float acc[8];
 #pragma unroll
@@ -135,14 +158,26 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
   // of this wavefront is loaded while the current one is consumed
   const int n_blocks = (end - start + KPB - 1) / KPB;
 
-  auto load_block = [&](int blk, u32x4_t (&kk)[kUnroll], u32x4_t (&vv)[kUnroll]) {
-    const int kbase = start + blk * KPB + kr;
+  // bit u of `valid` is cleared when load u's block id is out of range
+  // (paged only); such keys score -inf
+  auto load_block = [&](int blk, u32x4_t (&kk)[kUnroll], u32x4_t (&vv)[kUnroll], unsigned& valid) {
+    const int kbase0 = start + blk * KPB;
+    valid = (1u << kUnroll) - 1;
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const int key = kbase + u * KPI;
-      if (key < end) {
-        kk[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(Kh + (size_t)key * D + c * 8));
-        vv[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(Vh + (size_t)key * D + c * 8));
+      const int key = kbase0 + u * KPI + kr;
+      size_t row = (size_t)key;
+      bool ok = true;
+      if (PAGED) {
+        // the KPI rows of load u lie in one block: key0 = kbase0 + u * KPI
+        const int id = ids[((kbase0 + u * KPI) >> log2_bs) - e_first];
+        ok = (unsigned)id < (unsigned)num_blocks;
+        if (!ok) valid &= ~(1u << u);
+        row = ((((size_t)(ok ? id : 0)) * H + h) << log2_bs) + (key & ((1 << log2_bs) - 1));
+      }
+      if (ok && key < end) {
+        kk[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(Kh + row * D + c * 8));
+        vv[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(Vh + row * D + c * 8));
       } else {
         kk[u] = u32x4_t{};
         vv[u] = u32x4_t{};
@@ -150,7 +185,8 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
     }
   };
 
-  auto process_block = [&](int blk, const u32x4_t (&kk)[kUnroll], const u32x4_t (&vv)[kUnroll]) {
+  auto process_block = [&](int blk, const u32x4_t (&kk)[kUnroll], const u32x4_t (&vv)[kUnroll],
+                           const unsigned valid) {
     const int kbase = start + blk * KPB + kr;
     float s[kUnroll];
     float mb = -INFINITY;
@@ -162,20 +198,21 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
 #pragma unroll
       for (int e = 0; e < 8; ++e) p = __builtin_fmaf(qv[e], kf[e], p);
       p = group_sum<CPR>(p);
-      s[u] = (kbase + u * KPI < end) ? p : -INFINITY;
+      s[u] = (kbase + u * KPI < end && ((valid >> u) & 1u)) ? p : -INFINITY;
       mb = fmaxf(mb, s[u]);
     }
     // block maximum across the wavefront's rows
 #pragma unroll
     for (int off = CPR; off < 64; off <<= 1) mb = fmaxf(mb, __shfl_xor(mb, off));
-    const float m_new = fmaxf(m, mb);  // finite: the block's first key is valid
-    const float alpha = __builtin_amdgcn_exp2f(m - m_new);  // 0 on the first block
+    const float m_new = fmaxf(m, mb);  // -inf only while every key so far was skipped
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m - m_use);  // 0 on the first block
     float ps = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] *= alpha;
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const float p = __builtin_amdgcn_exp2f(s[u] - m_new);  // 0 for keys past the chunk
+      const float p = __builtin_amdgcn_exp2f(s[u] - m_use);  // 0 for keys past the chunk
       ps += p;
       float vf[8];
       bf16x8_to_f32(vv[u], vf);
@@ -187,14 +224,15 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
   };
 
   u32x4_t ka[kUnroll], va[kUnroll], kn[kUnroll], vn[kUnroll];
+  unsigned oka = 0, okn = 0;
   int blk = wave;
-  if (blk < n_blocks) load_block(blk, ka, va);
+  if (blk < n_blocks) load_block(blk, ka, va, oka);
   for (; blk < n_blocks; blk += 2 * kDecWaves) {
-    if (blk + kDecWaves < n_blocks) load_block(blk + kDecWaves, kn, vn);
-    process_block(blk, ka, va);
+    if (blk + kDecWaves < n_blocks) load_block(blk + kDecWaves, kn, vn, okn);
+    process_block(blk, ka, va, oka);
     if (blk + kDecWaves >= n_blocks) break;
-    if (blk + 2 * kDecWaves < n_blocks) load_block(blk + 2 * kDecWaves, ka, va);
-    process_block(blk + kDecWaves, kn, vn);
+    if (blk + 2 * kDecWaves < n_blocks) load_block(blk + 2 * kDecWaves, ka, va, oka);
+    process_block(blk + kDecWaves, kn, vn, okn);
   }
 
   // wavefront totals: sum over the row groups (lanes with the same slice c)
@@ -226,14 +264,15 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
     f[w] = (mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw - M);
     L2 += f[w] * wstate[w][1];
   }
-  const float inv = 1.f / L2;
+  // a chunk whose keys were all skipped (paged, invalid ids) is empty
+  const float inv = L2 > 0.f ? 1.f / L2 : 0.f;
   for (int e = tid; e < D; e += kThreads) {
     float o = 0.f;
 #pragma unroll
     for (int w = 0; w < kDecWaves; ++w) o += f[w] * wacc[w][e];
     part_o[out * D + e] = o * inv;
   }
-  if (tid == 0) part_lse[out] = (M + __log2f(L2)) * kLn2;
+  if (tid == 0) part_lse[out] = L2 > 0.f ? (M + __log2f(L2)) * kLn2 : -INFINITY;
 }
 
 constexpr int kCombineThreads = 256;
@@ -296,10 +335,16 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(
 
 template <int D>
 hipError_t launch(const DecodeArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_split_kernel<D>), dim3(a.S, a.H, a.B), dim3(kThreads), 0, stream,
-                     static_cast<const __bf16*>(a.q), static_cast<const __bf16*>(a.K),
-                     static_cast<const __bf16*>(a.V), a.Lkv, a.part_o, a.part_lse, a.H, a.S,
-                     a.capacity, a.scale);
+  if (a.table != nullptr)
+    hipLaunchKernelGGL((decode_split_kernel<D, true>), dim3(a.S, a.H, a.B), dim3(kThreads), 0, stream,
+                       static_cast<const __bf16*>(a.q), static_cast<const __bf16*>(a.K),
+                       static_cast<const __bf16*>(a.V), a.Lkv, a.part_o, a.part_lse, a.H, a.S, 0,
+                       a.scale, a.table, a.max_blocks, a.log2_bs, a.num_blocks);
+  else
+    hipLaunchKernelGGL((decode_split_kernel<D, false>), dim3(a.S, a.H, a.B), dim3(kThreads), 0, stream,
+                       static_cast<const __bf16*>(a.q), static_cast<const __bf16*>(a.K),
+                       static_cast<const __bf16*>(a.V), a.Lkv, a.part_o, a.part_lse, a.H, a.S,
+                       a.capacity, a.scale, nullptr, 0, 0, 0);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(a.H, a.B), dim3(kCombineThreads), 0, stream, a.part_o,

@@ -28,6 +28,12 @@ constexpr int kF32BC = 64;
 // to a multiple of kDecChunkAlign tokens.
 constexpr int kDecWaves = 4;
 constexpr int kDecChunkAlign = 64;
+// Paged decode: block ids one split workgroup stages in LDS (the host picks
+// split counts so that no chunk spans more blocks), and the block sizes
+// accepted (powers of two).
+constexpr int kPagedIdsPerChunk = 2048;
+constexpr int kPagedMinBlock = 16;
+constexpr int kPagedMaxBlock = 65536;
 
 struct FwdArgs {
   const void* Q;
@@ -53,6 +59,9 @@ struct DecodeArgs {
   int B, H, S;
   int capacity;     // 0 = packed
   float scale;
+  // paged cache (table != nullptr): K/V are pools [num_blocks, H, 2^log2_bs, d]
+  const int32_t* table = nullptr;  // [B, max_blocks]
+  int max_blocks = 0, log2_bs = 0, num_blocks = 0;
 };
 
 // Launchers: enqueue on `stream`, return hipGetLastError().
@@ -87,6 +96,12 @@ inline int64_t fwd_units(int B, int H, int N, int causal) {
 // hardware overlap one workgroup's start with another's end.
 inline int64_t fwd_grid(int64_t units, int causal, int cus) {
   return causal ? (units < cus ? units : cus) : units;
+}
+
+// Blocks a chunk of at most chunk_tokens tokens can touch when chunks start
+// at multiples of kDecChunkAlign and blocks hold block_size tokens.
+inline int64_t paged_blocks_per_chunk(int64_t chunk_tokens, int block_size) {
+  return ceil_div64(chunk_tokens, block_size) + 1;
 }
 
 // Decode chunk length for a sequence of `len` tokens split `S` ways.

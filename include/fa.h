@@ -146,6 +146,45 @@ int fa_decode_ex(const void* q, const void* Kcache, const void* Vcache, void* o,
  * count on the current device.  Returns 0 for invalid arguments. */
 size_t fa_decode_workspace_bytes(int B, int H, int d, int num_splits);
 
+/*
+ * fa_decode_paged -- Flash-Decoding against a KV cache kept in fixed-size
+ * blocks and read through a block table ([L18] section 7.3: blocks of a fixed
+ * number of tokens, a table from each sequence's logical blocks to physical
+ * ones, attention computed block by block and merged with the (m, l, o) state
+ * of section 2.3).
+ *   q, o, lse_out, Lkv, scale : as in fa_decode_ex
+ *   Kpool, Vpool : device bf16 [num_blocks, H, block_size, d]; physical
+ *             block p holds block_size consecutive tokens of every head
+ *   block_table : device int32 [B, max_blocks], row-major; entry [b, i] is
+ *             the physical block of tokens i*block_size .. (i+1)*block_size-1
+ *             of sequence b.  Only entries i < ceil(Lkv[b] / block_size) are
+ *             read.  An entry outside [0, num_blocks) is never dereferenced:
+ *             its tokens are skipped (they contribute nothing).
+ *   Lkv     : device int32 [B]; lengths above max_blocks * block_size are
+ *             clamped to it
+ *   block_size : a power of two in [16, 65536]
+ *   num_splits : chunks per (b, h), 0 = automatic (fa_decode's rule, raised
+ *             until no chunk spans more than 2048 blocks); an explicit count
+ *             that lets a chunk span more is rejected (FA_ERR_UNSUPPORTED).
+ *   workspace : caller-owned device memory of at least
+ *             fa_decode_workspace_bytes(B, H, d, S) bytes for the split count
+ *             S that fa_decode_paged_splits reports, 256-byte aligned; or NULL
+ *             with workspace_bytes = 0 to use the library's workspace (as
+ *             fa_decode: grown with hipMalloc outside stream capture only).
+ * Identical keys give results identical to fa_decode_ex on a contiguous
+ * cache with the same split count.  Errors: as fa_decode_ex.
+ */
+int fa_decode_paged(const void* q, const void* Kpool, const void* Vpool, void* o, float* lse_out,
+                    int B, int H, const int32_t* block_table, int max_blocks, const int32_t* Lkv,
+                    int num_blocks, int block_size, int d, int num_splits, float scale,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* The split count fa_decode_paged uses for these arguments (resolving
+ * num_splits = 0 on the current device, or for 256 compute units without
+ * one); 0 if the arguments are invalid or no count keeps every chunk within
+ * 2048 blocks. */
+int fa_decode_paged_splits(int B, int H, int max_blocks, int block_size, int num_splits);
+
 /* Host-only launch planning (no HIP call; usable without a GPU).
  * fa_fwd_plan: tile geometry and the exact number of tiles fa_fwd visits.
  * Causal fa_fwd runs a persistent grid of one workgroup per compute unit,

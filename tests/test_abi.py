@@ -204,3 +204,51 @@ def test_fwd_causal_pairs_balance_work():
     assert work == {r * (T + 1)}
     assert p["work_units"] == len(units)
     assert p["tiles_visited"] == sum(per_tile)
+
+
+def _paged(q=A, Kp=2 * A, Vp=3 * A, o=4 * A, lse=None, B=2, H=4, table=5 * A, max_blocks=64, Lkv=6 * A,
+           num_blocks=100, bs=16, d=128, splits=8, scale=0.1, ws=None, ws_bytes=0):
+    return _fa().lib.fa_decode_paged(q, Kp, Vp, o, lse, B, H, table, max_blocks, Lkv, num_blocks, bs, d,
+                                     splits, ctypes.c_float(scale), ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize(
+    "kw,status,msg",
+    [
+        (dict(table=None), -1, "block_table"),
+        (dict(table=5 * A + 2), -1, "block_table misaligned"),
+        (dict(bs=8), -1, "power of two"),
+        (dict(bs=48), -1, "power of two"),
+        (dict(bs=0), -1, "power of two"),
+        (dict(max_blocks=0), -1, ">= 1"),
+        (dict(num_blocks=0), -1, ">= 1"),
+        (dict(d=96), -2, "not supported"),
+        (dict(splits=-1), -1, "num_splits"),
+        (dict(scale=0.0), -1, "scale"),
+        (dict(max_blocks=100000, splits=8), -2, "more splits"),
+        (dict(ws=7 * A + 16, ws_bytes=1 << 20), -5, "aligned"),
+        (dict(ws=7 * A, ws_bytes=16), -5, "too small"),
+        (dict(ws=None, ws_bytes=64), -5, "nonzero"),
+        (dict(o=5 * A), -1, "overlaps"),
+    ],
+)
+def test_decode_paged_rejects_invalid_arguments(kw, status, msg):
+    fa = _fa()
+    assert _paged(**kw) == status
+    assert msg in fa.last_error()
+
+
+def test_decode_paged_split_count():
+    """Automatic splits follow fa_decode's rule (planned for 256 compute
+    units without a device) and are raised until no chunk of the longest
+    possible sequence spans more than 2048 blocks."""
+    fa = _fa()
+    assert fa.fa_decode_paged_splits(1, 32, 2048, 16, 0) == 8
+    s = fa.fa_decode_paged_splits(1, 32, 100000, 16, 0)
+    assert s > 8
+    chunk = fa.fa_decode_chunk_tokens(100000 * 16, s)
+    assert -(-chunk // 16) + 1 <= 2048
+    assert -(-fa.fa_decode_chunk_tokens(100000 * 16, s // 2) // 16) + 1 > 2048
+    assert fa.fa_decode_paged_splits(1, 32, 100000, 16, 8) == 0
+    assert fa.fa_decode_paged_splits(1, 32, 64, 12, 8) == 0
+    assert fa.fa_decode_paged_splits(2, 4, 64, 16, 5) == 5

@@ -1,0 +1,196 @@
+"""Parity of the paged-KV decode (fa_decode_paged, through the C ABI) with the
+float64 oracle ("CMU 10-423 Lecture 18" notes, section 7.3) and with the
+contiguous-cache decode.
+
+Bars as for decode: max|do| <= 2e-2 and max|dlse| <= 2e-3 against the oracle;
+on identical keys the paged and contiguous kernels give identical bits, since
+chunking, per-key arithmetic and the combine are the same.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+BF16_O, BF16_L = 2e-2, 2e-3
+
+
+def _fa():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import exact_io_aware_02_amd as fa
+
+    return fa
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+
+
+def _host(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def _cfg(B, H, d, seed, block_size, vscale=1.0, spare=5):
+    return dict(kind="paged", B=B, H=H, d=d, dtype="bf16", vscale=vscale, seed=seed, block_size=block_size,
+                spare_blocks=spare)
+
+
+def _gather_heads(pool, table_row, length, block_size, h):
+    """[length, d] float64 of head h gathered on the device (only the used
+    blocks travel to the host)."""
+    nb = oracle.blocks_of(length, block_size)
+    if nb == 0:
+        return np.zeros((0, pool.shape[3]))
+    ids = torch.as_tensor(np.asarray(table_row[:nb], dtype=np.int64), device=pool.device)
+    blk = pool.index_select(0, ids)[:, h]  # [nb, bs, d]
+    return _host(blk.reshape(-1, pool.shape[3]))[:length]
+
+
+def _compare(q, Kp, Vp, table, lengths, o, lse, scale, heads=None):
+    B, H, d = q.shape
+    bs = Kp.shape[2]
+    heads = heads if heads is not None else [(b, h) for b in range(B) for h in range(H)]
+    dO = dL = 0.0
+    for b, h in heads:
+        k = _gather_heads(Kp, table[b], int(lengths[b]), bs, h)
+        v = _gather_heads(Vp, table[b], int(lengths[b]), bs, h)
+        o_ref, l_ref = oracle.decode_ref(_host(q[b, h]), k, v, scale)
+        dO = max(dO, float(np.abs(_host(o[b, h]) - o_ref).max()))
+        if lse is not None:
+            l_dev = float(lse[b, h])
+            if l_ref == -np.inf:
+                assert l_dev == -np.inf
+            else:
+                dL = max(dL, abs(l_dev - l_ref))
+    return dO, dL
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("bs", [16, 64, 256])
+def test_paged_small_vs_oracle(d, bs):
+    fa = _fa()
+    _say("paged small", d, bs)
+    lengths = np.array([1, 17, 300, 0, 4097], dtype=np.int64)
+    q, Kp, Vp, table, lengths = synth.paged_inputs(_cfg(len(lengths), 3, d, 40 + bs, bs), "cuda", lengths=lengths)
+    B, H, _ = q.shape
+    Lkv = torch.tensor(lengths, dtype=torch.int32, device="cuda")
+    tb = torch.tensor(table, dtype=torch.int32, device="cuda")
+    o = torch.empty_like(q)
+    lse = torch.empty(B, H, device="cuda")
+    scale = 1.0 / np.sqrt(d)
+    for splits in (1, 3, 0):
+        fa.fa_decode_paged(q, Kp, Vp, o, tb, Lkv, lse_out=lse, num_splits=splits)
+        torch.cuda.synchronize()
+        dO, dL = _compare(q, Kp, Vp, table, lengths, o, lse, scale)
+        assert dO <= BF16_O and dL <= BF16_L, (splits, dO, dL)
+        assert torch.all(o[3] == 0) and torch.all(torch.isneginf(lse[3]))
+
+
+def test_paged_matches_contiguous_bitwise():
+    """The same keys behind a block table and packed contiguously give the
+    same bits (same split count, same chunks, same arithmetic)."""
+    fa = _fa()
+    _say("paged vs contiguous")
+    B, H, d, bs, S = 3, 4, 128, 16, 6
+    lengths = np.array([100, 0, 1000], dtype=np.int64)
+    cfg = dict(kind="decode", B=B, H=H, d=d, dtype="bf16", vscale=2.0, seed=77)
+    q, Kc, Vc, lengths = synth.decode_inputs(cfg, "cuda", lengths=lengths)
+    table, num_blocks = synth.block_table(lengths, bs, spare_blocks=3, seed=78)
+    Kp = torch.zeros(num_blocks, H, bs, d, dtype=torch.bfloat16, device="cuda")
+    Vp = torch.zeros_like(Kp)
+    offs = synth.packed_offsets(lengths, H, d)
+    for b in range(B):
+        L = int(lengths[b])
+        nb = oracle.blocks_of(L, bs)
+        if nb == 0:
+            continue
+        for src, dst in ((Kc, Kp), (Vc, Vp)):
+            seq = src[offs[b]: offs[b] + H * L * d].view(H, L, d)
+            pad = torch.zeros(H, nb * bs, d, dtype=seq.dtype, device="cuda")
+            pad[:, :L] = seq
+            ids = torch.as_tensor(table[b, :nb].astype(np.int64), device="cuda")
+            dst[ids] = pad.view(H, nb, bs, d).permute(1, 0, 2, 3)
+    Lkv = torch.tensor(lengths, dtype=torch.int32, device="cuda")
+    ws = torch.empty(fa.fa_decode_workspace_bytes(B, H, d, S), dtype=torch.uint8, device="cuda")
+    o1, o2 = torch.empty_like(q), torch.empty_like(q)
+    l1, l2 = torch.empty(B, H, device="cuda"), torch.empty(B, H, device="cuda")
+    fa.fa_decode_ex(q, Kc, Vc, o1, Lkv, ws, lse_out=l1, num_splits=S)
+    fa.fa_decode_paged(q, Kp, Vp, o2, torch.tensor(table, device="cuda"), Lkv, lse_out=l2, num_splits=S,
+                       workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+    assert torch.equal(l1, l2)
+
+
+def test_paged_skips_invalid_block_ids():
+    """Table entries outside [0, num_blocks) are never dereferenced; their
+    tokens contribute nothing (the decode over the remaining tokens)."""
+    fa = _fa()
+    _say("paged invalid ids")
+    B, H, d, bs = 2, 2, 128, 16
+    lengths = np.array([80, 40], dtype=np.int64)  # 5 and 3 blocks
+    q, Kp, Vp, table, lengths = synth.paged_inputs(_cfg(B, H, d, 90, bs), "cuda", lengths=lengths)
+    num_blocks = Kp.shape[0]
+    bad = table.copy()
+    bad[0, 1] = -1
+    bad[0, 3] = num_blocks + 1000
+    bad[1, 0] = -7
+    Lkv = torch.tensor(lengths, dtype=torch.int32, device="cuda")
+    o = torch.empty_like(q)
+    lse = torch.empty(B, H, device="cuda")
+    fa.fa_decode_paged(q, Kp, Vp, o, torch.tensor(bad, device="cuda"), Lkv, lse_out=lse, num_splits=2)
+    torch.cuda.synchronize()
+    scale = 1.0 / np.sqrt(d)
+    for b in range(B):
+        keep = [i for i in range(oracle.blocks_of(lengths[b], bs)) if 0 <= bad[b, i] < num_blocks]
+        for h in range(H):
+            ks, vs = [], []
+            for i in keep:
+                n = min(bs, int(lengths[b]) - i * bs)
+                ks.append(_host(Kp[int(bad[b, i]), h, :n]))
+                vs.append(_host(Vp[int(bad[b, i]), h, :n]))
+            o_ref, l_ref = oracle.decode_ref(_host(q[b, h]), np.concatenate(ks), np.concatenate(vs), scale)
+            assert float(np.abs(_host(o[b, h]) - o_ref).max()) <= BF16_O
+            assert abs(float(lse[b, h]) - l_ref) <= BF16_L
+
+
+def test_paged_internal_workspace_and_determinism():
+    fa = _fa()
+    _say("paged workspace")
+    lengths = np.array([5000, 123], dtype=np.int64)
+    q, Kp, Vp, table, lengths = synth.paged_inputs(_cfg(2, 8, 128, 95, 32), "cuda", lengths=lengths)
+    Lkv = torch.tensor(lengths, dtype=torch.int32, device="cuda")
+    tb = torch.tensor(table, device="cuda")
+    B, H, d = q.shape
+    S = fa.fa_decode_paged_splits(B, H, table.shape[1], 32, 0)
+    assert S > 0
+    ws = torch.empty(fa.fa_decode_workspace_bytes(B, H, d, S), dtype=torch.uint8, device="cuda")
+    o1, o2 = torch.empty_like(q), torch.empty_like(q)
+    fa.fa_decode_paged(q, Kp, Vp, o1, tb, Lkv)
+    fa.fa_decode_paged(q, Kp, Vp, o2, tb, Lkv, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+
+
+def test_decode_paged_workload_sampled_heads():
+    """The decode_paged workload at full size (decode_varlen's lengths, 16
+    tokens per block, blocks scattered by a seeded permutation), in the
+    launch configuration the bench times; sampled heads against the oracle."""
+    fa = _fa()
+    cfg = synth.WORKLOADS["decode_paged"]
+    _say("decode_paged", cfg)
+    q, Kp, Vp, table, lengths = synth.paged_inputs("decode_paged", "cuda")
+    Lkv = torch.tensor(lengths, dtype=torch.int32, device="cuda")
+    o = torch.empty_like(q)
+    B, H, d = q.shape
+    lse = torch.empty(B, H, device="cuda")
+    fa.fa_decode_paged(q, Kp, Vp, o, torch.tensor(table, device="cuda"), Lkv, lse_out=lse)
+    torch.cuda.synchronize()
+    heads = [(b, h) for b in range(B) for h in (0, 17, 31)]
+    dO, dL = _compare(q, Kp, Vp, table, lengths, o, lse, 1.0 / np.sqrt(d), heads=heads)
+    assert dO <= BF16_O and dL <= BF16_L, (dO, dL)
