@@ -133,6 +133,34 @@ def test_bf16_small_shapes(N, d, causal):
     assert dO <= BF16_O and dL <= BF16_L, (dO, dL)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N", [17, 100, 1000])
+def test_bf16_ragged_tail_reads_nothing_past_the_head(N, d):
+    """Keys past N are not part of the problem: their rows must read as
+    zeros, never as whatever memory follows the head.  Q, K, V are views at
+    the start of one allocation whose remainder holds NaN, so any read past
+    the last head would turn into NaN in O (a NaN value row times a zero
+    weight is still NaN); the reads stay inside the allocation either way."""
+    fa = _fa()
+    _say("bf16 ragged tail guard", N, d)
+    shape = (1, 3, N, d)
+    n = math.prod(shape)
+    outs = []
+    for t in range(3):
+        buf = torch.full((n + 128 * d,), float("nan"), device="cuda", dtype=torch.bfloat16)
+        buf[:n] = synth.torch_normal(500 + t, shape, "cuda", "bf16").reshape(-1)
+        outs.append(buf[:n].view(shape))
+    Q, K, V = outs
+    O = torch.empty_like(Q)
+    L = torch.empty(shape[:3], device="cuda")
+    for causal in (False, True):
+        fa.fa_fwd(Q, K, V, O, L, causal=causal)
+        torch.cuda.synchronize()
+        assert not torch.isnan(O).any() and not torch.isnan(L).any(), causal
+        dO, dL = _prefill_compare(Q, K, V, O, L, 1 / math.sqrt(d), causal)
+        assert dO <= BF16_O and dL <= BF16_L, (causal, dO, dL)
+
+
 def test_bf16_large_values_and_scale():
     """Scores with a wide spread (values x4, scale 0.5) exercise the running
     maximum and the alpha rescale across many tiles."""
