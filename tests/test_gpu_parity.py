@@ -161,6 +161,27 @@ def test_bf16_ragged_tail_reads_nothing_past_the_head(N, d):
         assert dO <= BF16_O and dL <= BF16_L, (causal, dO, dL)
 
 
+@pytest.mark.parametrize("B,H,N", [(2, 200, 50), (1, 300, 300), (1, 520, 129), (3, 100, 700)])
+def test_bf16_causal_many_items_per_workgroup(B, H, N):
+    """Causal launches keep at most one workgroup per compute unit, so with
+    many heads each workgroup runs a sequence of query tiles, staging the
+    next tile's Q and first K/V tiles during the current one and storing the
+    previous tile's output inside the next.  Covers single-tile items (N <=
+    64: every step is an item boundary) and mixes of long and short items;
+    every head and row is compared."""
+    fa = _fa()
+    _say("bf16 causal many items", B, H, N)
+    shape = (B, H, N, 128)
+    Q, K, V = (synth.torch_normal(700 + t, shape, "cuda", "bf16") for t in range(3))
+    O = torch.full_like(Q, float("nan"))
+    L = torch.full(shape[:3], float("nan"), device="cuda")
+    fa.fa_fwd(Q, K, V, O, L, causal=True)
+    torch.cuda.synchronize()
+    assert not torch.isnan(O).any() and not torch.isnan(L).any()
+    dO, dL = _prefill_compare(Q, K, V, O, L, 1 / math.sqrt(128), True)
+    assert dO <= BF16_O and dL <= BF16_L, (dO, dL)
+
+
 def test_bf16_large_values_and_scale():
     """Scores with a wide spread (values x4, scale 0.5) exercise the running
     maximum and the alpha rescale across many tiles."""
