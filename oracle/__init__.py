@@ -18,8 +18,9 @@ Sources (three web pages on one subject; cited by title and section):
   sequence partitioning, per-chunk partials, log-sum-exp reduction).
 * "CMU 10-423 Lecture 18: FlashAttention & efficient decoding" notes,
   sections 2.1-2.3 (online softmax, (m, l, o) merging), 3.2-3.4 (tiled forward,
-  FA-2 loop order), 4.1 and 4.3 (IO counts, causal tile skipping), 7.3 (KV
-  cache in blocks behind a block table) and Exercises 1-4.
+  FA-2 loop order), 4.1 and 4.3 (IO counts, causal tile skipping), 5.3 (the
+  FlashAttention backward by recomputation), 7.3 (KV cache in blocks behind
+  a block table) and Exercises 1-4.
 
 Modules:
 
@@ -29,6 +30,9 @@ Modules:
   merge, and the Flash-Decoding combine of (O^(k), m^(k), l^(k)) partials.
 * ``tiled``      -- Algorithm 1 of "Infra: Flash Attention" taken step by step
   with tile counters, and the closed-form IO counts of the lecture notes.
+* ``backward``   -- gradients dQ, dK, dV of exact attention: the plain
+  definition through P, and the tiled recomputation from O and L
+  ("Infra: Flash Attention", "Backward and recomputation").
 * ``paged``      -- decode against a KV cache kept in fixed-size blocks and
   read through a block table (lecture notes, section 7.3), both as the plain
   definition on the gathered cache and block by block with (m, l, u) merges.
@@ -49,6 +53,7 @@ from .online import (
 )
 from .tiled import tiled_ref, io_standard, io_fa2, io_fa1_main, causal_tile_count
 from .paged import blocks_of, gather_paged, decode_paged_ref, decode_paged_blockwise
+from .backward import attention_backward, attention_backward_ref, attention_backward_tiled
 
 __all__ = [
     "attention_ref",
@@ -69,4 +74,7 @@ __all__ = [
     "gather_paged",
     "decode_paged_ref",
     "decode_paged_blockwise",
+    "attention_backward",
+    "attention_backward_ref",
+    "attention_backward_tiled",
 ]

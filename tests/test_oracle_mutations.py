@@ -182,3 +182,49 @@ def test_blockwise_without_rescaling_is_caught(monkeypatch):
 
     monkeypatch.setattr(pgd, "merge", naive_merge)
     assert _fails(ppins.test_worked_example_section73)
+
+
+# --------------------------------------------------------------------------
+# backward oracle
+# --------------------------------------------------------------------------
+
+import oracle.backward as bwd  # noqa: E402
+import tests.test_oracle_backward as bpins  # noqa: E402
+
+
+def test_backward_D_without_P_is_caught(monkeypatch):
+    monkeypatch.setattr(bwd, "_row_D", lambda p, h: h.sum(axis=1))
+    assert _fails(bpins.test_backward_vs_torch_autograd, 37, 16, 0.3, False)
+    assert _fails(bpins.test_backward_closed_forms, False)
+
+
+def test_backward_dropped_D_is_caught(monkeypatch):
+    monkeypatch.setattr(bwd, "_score_grad", lambda p, h, D: p * h)
+    assert _fails(bpins.test_backward_vs_finite_differences, False)
+
+
+def test_backward_flipped_score_gradient_sign_is_caught(monkeypatch):
+    monkeypatch.setattr(bwd, "_score_grad", lambda p, h, D: p * (D[:, None] - h))
+    assert _fails(bpins.test_backward_vs_torch_autograd, 64, 64, 0.125, True)
+
+
+def test_backward_unnormalised_probabilities_are_caught(monkeypatch):
+    monkeypatch.setattr(bwd, "_softmax_rows", lambda s: np.exp(s - s.max(axis=1)[:, None]))
+    assert _fails(bpins.test_backward_vs_torch_autograd, 37, 16, 0.3, True)
+
+
+def test_backward_tiled_with_log2_lse_is_caught(monkeypatch):
+    orig = bwd.attention_backward_tiled
+
+    def bad(q, k, v, do, scale, br, bc, causal=False, o=None, lse=None):
+        o_, l_ = oracle.attention_rows(q, k, v, scale, causal=causal)
+        return orig(q, k, v, do, scale, br, bc, causal=causal, o=o_, lse=l_ / np.log(2.0))
+
+    monkeypatch.setattr(oracle, "attention_backward_tiled", bad)
+    assert _fails(bpins.test_backward_tiled_equals_definition, 16, 8, False)
+
+
+def test_backward_dropped_causal_mask_is_caught(monkeypatch):
+    orig_scores = bwd._masked_scores
+    monkeypatch.setattr(bwd, "_masked_scores", lambda q, k, scale, causal, q_pos: orig_scores(q, k, scale, False, q_pos))
+    assert _fails(bpins.test_backward_vs_torch_autograd, 37, 16, 0.3, True)
