@@ -1,5 +1,5 @@
-"""Exact attention forward (FlashAttention) and Flash-Decoding for AMD
-MI355X (gfx950).
+"""Exact attention forward (FlashAttention), its backward, and Flash-Decoding
+for AMD MI355X (gfx950).
 
 The compute lives in libfa.so (HIP kernels behind the C ABI of include/fa.h);
 this package is its ctypes binding.  Build the library in-tree with
@@ -16,6 +16,8 @@ from ._binding import (  # noqa: F401
     FA_ERR_NOMEM,
     FA_ERR_WORKSPACE,
     LIB_PATH,
+    fa_bwd,
+    fa_bwd_workspace_bytes,
     fa_decode,
     fa_decode_chunk_tokens,
     fa_decode_ex,

@@ -65,6 +65,8 @@ def _load():
         "fa_fwd": (I, [P, P, P, P, P, I, I, I, I, I, F, P]),
         "fa_fwd_f32": (I, [P, P, P, P, P, I, I, I, I, I, F, P]),
         "fa_decode": (I, [P, P, P, P, I, I, P, I, I, P]),
+        "fa_bwd": (I, [P, P, P, P, P, P, P, P, P, I, I, I, I, I, F, P, Z, P]),
+        "fa_bwd_workspace_bytes": (Z, [I, I, I]),
         "fa_decode_ex": (I, [P, P, P, P, P, I, I, P, I, I, I, F, P, Z, P]),
         "fa_decode_workspace_bytes": (Z, [I, I, I, I]),
         "fa_decode_paged": (I, [P, P, P, P, P, I, I, P, I, P, I, I, I, I, F, P, Z, P]),
@@ -90,6 +92,8 @@ lib = _load()
 EXPORTED = (
     "fa_fwd",
     "fa_fwd_f32",
+    "fa_bwd",
+    "fa_bwd_workspace_bytes",
     "fa_decode",
     "fa_decode_ex",
     "fa_decode_workspace_bytes",
@@ -190,6 +194,29 @@ def fa_fwd(Q, K, V, O, L=None, causal=False, scale=None, stream=None):
     _check(lib.fa_fwd(_ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(L), B, H, N, d, int(causal),
                       float(scale), _stream_ptr(stream)))
     return O, L
+
+
+def fa_bwd_workspace_bytes(B, H, N):
+    return lib.fa_bwd_workspace_bytes(int(B), int(H), int(N))
+
+
+def fa_bwd(Q, K, V, O, dO, L, dQ, dK, dV, causal=False, scale=None, workspace=None, stream=None):
+    """Gradients dQ, dK, dV (bf16 [B, H, N, d], overwritten) of the forward
+    that produced O and L from Q, K, V, given dO.  workspace: a device tensor
+    of at least fa_bwd_workspace_bytes(B, H, N) bytes, or None for the
+    library's internal one."""
+    import torch
+
+    B, H, N, d = Q.shape
+    for t, n in ((Q, "Q"), (K, "K"), (V, "V"), (O, "O"), (dO, "dO"), (dQ, "dQ"), (dK, "dK"), (dV, "dV")):
+        _expect(t, torch.bfloat16, (B, H, N, d), n)
+    _expect(L, torch.float32, (B, H, N), "L")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    ws, wsb = (None, 0) if workspace is None else (_ptr(workspace), workspace.numel() * workspace.element_size())
+    _check(lib.fa_bwd(_ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(dO), _ptr(L), _ptr(dQ), _ptr(dK), _ptr(dV), B, H, N,
+                      d, int(causal), float(scale), ws, wsb, _stream_ptr(stream)))
+    return dQ, dK, dV
 
 
 def fa_fwd_f32(Q, K, V, O, L=None, causal=False, scale=None, stream=None):

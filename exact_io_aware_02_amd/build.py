@@ -21,11 +21,15 @@ INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libfa.so")
 
-SOURCES = ["fa_api.hip", "fa_fwd_bf16.hip", "fa_fwd_f32.hip", "fa_decode.hip"]
+SOURCES = ["fa_api.hip", "fa_fwd_bf16.hip", "fa_fwd_f32.hip", "fa_decode.hip", "fa_bwd_bf16.hip"]
 # NaN inputs are outside the contract of the bf16 kernels; without NaN
 # semantics fmaxf needs no canonicalisation and fuses into v_max3_f32.
 # Infinities stay honoured (masked scores are -inf).
-PER_SOURCE_FLAGS = {"fa_fwd_bf16.hip": ["-fno-honor-nans"], "fa_decode.hip": ["-fno-honor-nans"]}
+PER_SOURCE_FLAGS = {
+    "fa_fwd_bf16.hip": ["-fno-honor-nans"],
+    "fa_decode.hip": ["-fno-honor-nans"],
+    "fa_bwd_bf16.hip": ["-fno-honor-nans"],
+}
 
 ARCH = "gfx950"
 # -packed-fp32-ops: keep the compiler from forming v_pk_{add,mul,fma}_f32

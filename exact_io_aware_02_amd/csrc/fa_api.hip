@@ -89,6 +89,39 @@ int check_decode(const void* q, const void* Kc, const void* Vc, const void* o, c
   return FA_OK;
 }
 
+// Backward checks.  The inputs Q, K, V, O, dO (bf16 [B, H, N, d]) and L
+// (fp32 [B, H, N]) may overlap each other; the outputs dQ, dK, dV may
+// overlap nothing.
+int check_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* L,
+              const void* dQ, const void* dK, const void* dV, int B, int H, int N, int d, int causal,
+              float scale) {
+  if (!Q || !K || !V || !O || !dO || !L || !dQ || !dK || !dV) return fail(FA_ERR_INVALID_ARG, "null tensor pointer");
+  if (B < 1 || H < 1 || N < 1) return fail(FA_ERR_INVALID_ARG, "B, H, N must be >= 1 (got %d, %d, %d)", B, H, N);
+  if (d < 1) return fail(FA_ERR_INVALID_ARG, "d must be >= 1 (got %d)", d);
+  if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "head dimension %d not supported (64 or 128)", d);
+  if (causal != 0 && causal != 1) return fail(FA_ERR_INVALID_ARG, "causal must be 0 or 1 (got %d)", causal);
+  if (!(isfinite(scale) && scale > 0.f)) return fail(FA_ERR_INVALID_ARG, "scale must be finite and > 0");
+  const void* t16[] = {Q, K, V, O, dO, dQ, dK, dV};
+  for (const void* p : t16)
+    if (!aligned(p, 16)) return fail(FA_ERR_INVALID_ARG, "Q, K, V, O, dO, dQ, dK, dV must be 16-byte aligned");
+  if (!aligned(L, 4)) return fail(FA_ERR_INVALID_ARG, "L must be 4-byte aligned");
+  const int64_t tiles = fa::ceil_div64(N, fa::kBwdQT < fa::kBwdKV ? fa::kBwdQT : fa::kBwdKV);
+  if ((int64_t)B * H * tiles > 0x7fffffffLL) return fail(FA_ERR_INVALID_ARG, "grid too large");
+  if ((int64_t)N * d * 2 > 0x7fffffffLL)
+    return fail(FA_ERR_INVALID_ARG, "one head of N x d elements must be under 2 GiB (N = %d)", N);
+  const size_t tb = (size_t)B * H * N * d * 2, lb = (size_t)B * H * N * sizeof(float);
+  const void* outs[] = {dQ, dK, dV};
+  const void* ins[] = {Q, K, V, O, dO};
+  for (int i = 0; i < 3; ++i) {
+    for (const void* in : ins)
+      if (overlap(outs[i], tb, in, tb)) return fail(FA_ERR_INVALID_ARG, "dQ, dK, dV must not overlap an input");
+    if (overlap(outs[i], tb, L, lb)) return fail(FA_ERR_INVALID_ARG, "dQ, dK, dV must not overlap L");
+    for (int j = i + 1; j < 3; ++j)
+      if (overlap(outs[i], tb, outs[j], tb)) return fail(FA_ERR_INVALID_ARG, "dQ, dK, dV must not overlap each other");
+  }
+  return FA_OK;
+}
+
 // Compute units assumed by the host-only planners (no device query).
 constexpr int kPlanCUs = 256;
 
@@ -322,6 +355,38 @@ int fa_decode(const void* q, const void* Kcache, const void* Vcache, void* o, in
   void* ws = nullptr;
   if ((st = internal_workspace(need, hs, &ws)) != FA_OK) return st;
   return decode_common(q, Kcache, Vcache, o, nullptr, B, H, Lkv, 0, d, S, scale, ws, hs);
+}
+
+size_t fa_bwd_workspace_bytes(int B, int H, int N) {
+  if (B < 1 || H < 1 || N < 1) return 0;
+  return align256((size_t)B * H * N * sizeof(float));
+}
+
+int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* L, void* dQ,
+           void* dK, void* dV, int B, int H, int N, int d, int causal, float scale, void* workspace,
+           size_t workspace_bytes, void* stream) {
+  int st = check_bwd(Q, K, V, O, dO, L, dQ, dK, dV, B, H, N, d, causal, scale);
+  if (st != FA_OK) return st;
+  const size_t need = fa_bwd_workspace_bytes(B, H, N);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  void* ws = workspace;
+  if (!workspace) {
+    if (workspace_bytes != 0) return fail(FA_ERR_WORKSPACE, "null workspace with nonzero workspace_bytes");
+    if ((st = internal_workspace(need, hs, &ws)) != FA_OK) return st;
+  } else {
+    if (!aligned(workspace, 256)) return fail(FA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    if (workspace_bytes < need)
+      return fail(FA_ERR_WORKSPACE, "workspace of %zu bytes is too small (%zu needed)", workspace_bytes, need);
+    const size_t tb = (size_t)B * H * N * d * 2, lb = (size_t)B * H * N * sizeof(float);
+    const void* tens[] = {Q, K, V, O, dO, dQ, dK, dV};
+    for (const void* p : tens)
+      if (overlap(workspace, need, p, tb)) return fail(FA_ERR_INVALID_ARG, "workspace overlaps a tensor");
+    if (overlap(workspace, need, L, lb)) return fail(FA_ERR_INVALID_ARG, "workspace overlaps L");
+  }
+  fa::BwdArgs a{Q, K, V, O, dO, L, dQ, dK, dV, static_cast<float*>(ws), B, H, N, causal, scale};
+  hipError_t e = fa::launch_bwd_bf16(a, d, hs);
+  if (e != hipSuccess) return hip_fail(e, "fa_bwd launch");
+  return ok();
 }
 
 int fa_decode_ex(const void* q, const void* Kcache, const void* Vcache, void* o, float* lse_out,

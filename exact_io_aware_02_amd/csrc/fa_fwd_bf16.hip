@@ -52,22 +52,14 @@
 //    head's K/V re-reads hit that XCD's L2; causal launches take the longest
 //    query tiles of each head first.
 
+#include "fa_device.h"
 #include "fa_internal.h"
 
 namespace fa {
 namespace {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef short i16x4_t __attribute__((ext_vector_type(4)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
-typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+using namespace dev;
 
-#define LDS_AS __attribute__((address_space(3)))
-
-constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleLog2 = 8.f;  // conditional-rescale threshold (base-2 exponent)
 constexpr int kThreads = kFwdWaves * 64;
 constexpr int kKB = kFwdBC / 32;  // 32-key blocks per KV tile (score accumulators)
@@ -90,87 +82,6 @@ struct Tile {
   static_assert(kLoads * 1024 == kBytes, "padded tiles must be whole KiB");
   static_assert(kLdsBytes == fwd_lds_bytes(D), "LDS size must match the planner");
 };
-
-// V rows are stored with the two 2-bit fields of (key mod 16) swapped, so
-// the 4 consecutive keys of one transposing read land 4 rows apart.
-__host__ __device__ constexpr int vrow_perm(int k) {
-  return (k & ~15) | ((k & 3) << 2) | ((k >> 2) & 3);
-}
-
-// Buffer resource (4 descriptor words) over `bytes` bytes at `base`, no
-// stride; loads at offsets past the end return zeros.
-__device__ __forceinline__ u32x4_t make_rsrc(const void* base, unsigned bytes) {
-  const unsigned long long a = (unsigned long long)base;
-  return u32x4_t{(unsigned)a, (unsigned)(a >> 32) & 0xFFFFu, bytes, 0x00020000u};
-}
-// 16 bytes per lane from rsrc[voff + soff] into LDS at lds + 16 * lane.
-// Issued as asm so the compiler does not order it against LDS reads of other
-// buffers (it cannot prove them disjoint and would drain the queue); every
-// wait for these loads is explicit (vmcnt) in the kernel.  The compiler's
-// hazard tracking does not look inside asm, so the leading s_nop 4 supplies
-// the wait states a buffer load needs after a VALU write of one of its SGPR
-// operands (v_readlane restoring a spilled descriptor: 5) and after the M0
-// write that sets the LDS address (1).
-__device__ __forceinline__ void load_lds16(u32x4_t rsrc, void LDS_AS* lds, unsigned voff, unsigned soff) {
-  asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
-               :
-               : "v"(voff), "s"(rsrc), "s"(soff), "{m0}"((unsigned)(size_t)lds)
-               : "memory");
-}
-
-__device__ __forceinline__ unsigned pack_bf16x2(float a, float b) {
-  bf16x2_t v = {(__bf16)a, (__bf16)b};
-  return __builtin_bit_cast(unsigned, v);
-}
-
-// max / sum with lane l^32 (the other key half of the same query); the swap
-// returns (x[l & 31], x[32 + (l & 31)]) in every lane.
-__device__ __forceinline__ float pair_max(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float pair_sum(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
-// Marks x as used at this point, so its computation is not sunk past it.
-// Input-only: the producing instruction stays the last writer of the
-// registers, so the compiler still inserts the wait states its readers need.
-// (The host pass parses kernel bodies too, and its target has no such
-// register class for 64-byte operands, hence the guard.)
-template <typename T>
-__device__ __forceinline__ void keep(const T& x) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  asm volatile("" ::"v"(x));
-#endif
-}
-
-// Workgroup barrier without the memory fence of __syncthreads (which would
-// drain every load in flight): the caller waits for what must have landed.
-// The empty asm statements keep the compiler from moving LDS accesses across.
-__device__ __forceinline__ void wg_barrier() {
-  __builtin_amdgcn_sched_barrier(0);
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_sched_barrier(0);
-}
-
-// Buffer offset of the 16 bytes that belong at byte `o` of a padded LDS tile;
-// a padding slot gets an offset past any buffer end (reads as zero, touches
-// no memory).
-template <int D>
-__device__ __forceinline__ unsigned lds_slot_source(int o, bool permuted) {
-  using T = Tile<D>;
-  const int p = o / T::kStride;
-  const int ch = (o - p * T::kStride) >> 4;
-  if (ch >= T::kChunks) return 0xFFFFFFF0u;
-  const int row = permuted ? vrow_perm(p) : p;
-  return (unsigned)(row * T::kRowBytes + ch * 16);
-}
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -197,8 +108,8 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ K
 #pragma unroll
   for (int p = 0; p < T::kLoadsPerWave; ++p) {
     const int o = (wave + p * kFwdWaves) * 1024 + lane * 16;
-    k_voff[p] = lds_slot_source<D>(o, false);
-    v_voff[p] = lds_slot_source<D>(o, true);
+    k_voff[p] = padded_source<D>(o, false);
+    v_voff[p] = padded_source<D>(o, true);
   }
   auto dma_tile = [&](const u32x4_t rsrc, const unsigned* voff, int tile, char LDS_AS* dst) {
     const unsigned soff = (unsigned)tile * kFwdBC * T::kRowBytes;
@@ -214,26 +125,10 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ K
   // ---- per-lane LDS read bases (everything else is a compile-time offset)
   // K fragment (A operand of S^T = K Q^T): row l32, chunk 2*ds + g
   const int k_base = l32 * T::kStride + g * 16;
-  // V^T fragment for key step ks, half t: keys ks*16 + 8t + 4g + k (k = 0..3)
-  // at stored rows ks*16 + 4k + 2t + g; lanes address dims 16*((lane>>4)&1) + 4*(lane&3)
-  const int v_base = (4 * ((lane & 15) >> 2) + g) * T::kStride +
-                     (((lane >> 4) & 1) * 16 + (lane & 3) * 4) * 2;
-  // A operand of U^T += V^T W^T for head-dimension block db and key step ks:
-  // two transposing reads (keys ks*16 + 8t + 4g + 0..3 for t = 0, 1)
-  auto v_frag = [&](const char LDS_AS* vb, int db, int ks) {
-    bf16x8_t a;
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (i16x4_t LDS_AS*)(vb + (ks * 16 + 2 * t) * T::kStride + db * 64));
-      const bf16x4_t v4 = __builtin_bit_cast(bf16x4_t, v);
-      a[4 * t + 0] = v4[0];
-      a[4 * t + 1] = v4[1];
-      a[4 * t + 2] = v4[2];
-      a[4 * t + 3] = v4[3];
-    }
-    return a;
-  };
+  // V^T fragment (A operand of U^T += V^T W^T) for head-dimension block db
+  // and key step ks: two transposing reads of keys ks*16 + 8t + 4g + 0..3
+  const int v_base = tr_lane_base<T::kStride>(lane);
+  auto v_frag = [&](const char LDS_AS* vb, int db, int ks) { return tr_frag<T::kStride>(vb, ks, db * 64); };
 
   const float c = scale * kLog2e;
   const float theta = kRescaleLog2 / c;  // threshold in raw score units

@@ -24,6 +24,20 @@ __host__ __device__ constexpr int fwd_lds_bytes(int d) { return 4 * kFwdBC * (2 
 constexpr int kF32BR = 64;
 constexpr int kF32BC = 64;
 
+// bf16 backward: wavefronts per workgroup (one per SIMD); the dK/dV kernel
+// gives each wavefront 32 keys (kBwdKV per workgroup) and walks query tiles
+// of kBwdQT rows; the dQ kernel gives each wavefront 32 queries (kBwdQ per
+// workgroup) and walks KV tiles of kBwdKT keys.  LDS: two buffers of
+// (Q tile, dO tile, 1 KiB of L, 1 KiB of D), resp. (K tile, V tile), rows
+// padded by 16 bytes.
+constexpr int kBwdWaves = 4;
+constexpr int kBwdKV = 32 * kBwdWaves;
+constexpr int kBwdQT = 64;
+constexpr int kBwdQ = 32 * kBwdWaves;
+constexpr int kBwdKT = 64;
+__host__ __device__ constexpr int bwd_dkdv_lds_bytes(int d) { return 2 * (2 * kBwdQT * (2 * d + 16) + 2 * 1024); }
+__host__ __device__ constexpr int bwd_dq_lds_bytes(int d) { return 2 * 2 * kBwdKT * (2 * d + 16); }
+
 // Decode split kernel: wavefronts per workgroup; chunk lengths are rounded up
 // to a multiple of kDecChunkAlign tokens.
 constexpr int kDecWaves = 4;
@@ -47,6 +61,22 @@ struct FwdArgs {
   int grid;  // bf16 prefill: persistent workgroups, 1 <= grid <= fwd_units
 };
 
+struct BwdArgs {
+  const void* Q;
+  const void* K;
+  const void* V;
+  const void* O;
+  const void* dO;
+  const float* L;
+  void* dQ;
+  void* dK;
+  void* dV;
+  float* Dws;  // [B, H, N] fp32 workspace: D_i = dO_i . O_i
+  int B, H, N;
+  int causal;
+  float scale;
+};
+
 struct DecodeArgs {
   const void* q;
   const void* K;
@@ -68,6 +98,7 @@ struct DecodeArgs {
 hipError_t launch_fwd_bf16(const FwdArgs& a, int d, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdArgs& a, int d, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, int d, hipStream_t stream);
+hipError_t launch_bwd_bf16(const BwdArgs& a, int d, hipStream_t stream);
 
 // Host-side tile bookkeeping used by both the planner and the launcher.
 __host__ __device__ inline int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }

@@ -1,12 +1,14 @@
 /*
- * fa.h -- exact attention forward (FlashAttention) and single-query
- * Flash-Decoding for AMD MI355X (gfx950).  C ABI.
+ * fa.h -- exact attention forward (FlashAttention), its backward by
+ * recomputation, and single-query Flash-Decoding for AMD MI355X (gfx950).
+ * C ABI.
  *
  * Sources, cited by page title and section:
  *  [FA]  "Infra: Flash Attention" (pufanyi.com blog): "Attention and scope"
  *        (S = Q K^T / sqrt(d), row softmax, O = P V), "Tiled computation and
  *        forward" (Algorithm 1, FlashAttention forward; boundary conditions),
- *        "Backward and recomputation" (L_i = m_i + log l_i), "Prefill and
+ *        "Backward and recomputation" (L_i = m_i + log l_i; recomputing P
+ *        from L) and the tiled-gradient section after it, "Prefill and
  *        decode".
  *  [FD]  airsota interview card "Efficient attention & FlashAttention"
  *        (science-depth M4-055), section 3 "Mathematical principles &
@@ -14,7 +16,8 @@
  *        chunks, one partial (O^(k), m^(k), l^(k)) per chunk, log-sum-exp
  *        reduction), section 4 (choice of the chunk count).
  *  [L18] "CMU 10-423 Lecture 18" notes: section 3.4 (FA-2 loop order),
- *        section 4.3 (causal masks skip whole tiles).
+ *        section 4.3 (causal masks skip whole tiles), section 5.3 (the
+ *        FlashAttention backward), section 7.3 (KV cache in blocks).
  *
  * Conventions shared by every entry point
  *  - Tensors are dense, row-major, with the head dimension d contiguous.
@@ -99,6 +102,40 @@ int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* L, int B
  */
 int fa_fwd_f32(const float* Q, const float* K, const float* V, float* O, float* L, int B,
                int H, int N, int d, int causal, float scale, void* stream);
+
+/*
+ * fa_bwd -- gradients of the FlashAttention forward by recomputation ([FA]
+ * "Backward and recomputation" and its tiled-gradient section; [L18]
+ * section 5.3).
+ *   Q, K, V : device bf16 [B, H, N, d], the forward's inputs
+ *   O, L    : the forward's outputs (bf16 [B, H, N, d] and fp32 [B, H, N],
+ *             natural-log log-sum-exp of the scaled scores) for the same Q,
+ *             K, V, causal and scale
+ *   dO      : device bf16 [B, H, N, d], the gradient of the loss w.r.t. O
+ *   dQ, dK, dV : device bf16 [B, H, N, d], fully overwritten:
+ *             D_i = dO_i . O_i, P_ij = exp(S_ij - L_i) with S = Q K^T scale
+ *             (causal: P_ij = 0 for j > i), dV = P^T dO, dS = P o (dO V^T -
+ *             D), dQ = scale dS K, dK = scale dS^T Q; each element rounded to
+ *             nearest-even from fp32
+ *   causal, scale : as in fa_fwd
+ *   workspace : device memory of at least fa_bwd_workspace_bytes(B, H, N)
+ *             bytes, 256-byte aligned, for D; or NULL with workspace_bytes = 0
+ *             to use the library's workspace of the (device, stream) (grown
+ *             with hipMalloc, so not while the stream is being captured)
+ * Arithmetic: bf16 MFMA products with fp32 accumulation; P and dS are rounded
+ * to bf16 as product operands; D, P, dP and dS are computed in fp32.  The
+ * result does not depend on timing (no atomics).  The inputs may overlap
+ * each other; the outputs may not overlap an input, L, the workspace or each
+ * other.  Errors: FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED (d), FA_ERR_WORKSPACE,
+ * FA_ERR_NOMEM, FA_ERR_HIP.
+ */
+int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* L,
+           void* dQ, void* dK, void* dV, int B, int H, int N, int d, int causal, float scale,
+           void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes fa_bwd needs (B * H * N floats, rounded up to 256);
+ * 0 for invalid arguments. */
+size_t fa_bwd_workspace_bytes(int B, int H, int N);
 
 /*
  * fa_decode -- Flash-Decoding of one query per (b, h) against a KV cache
@@ -198,8 +235,8 @@ int fa_fwd_plan(int B, int H, int N, int d, int causal, fa_fwd_plan_t* out);
 int fa_decode_plan(int B, int H, int d, int num_splits, fa_decode_plan_t* out);
 int fa_decode_chunk_tokens(int kv_len, int num_splits);
 
-/* Frees fa_decode's internal workspaces (synchronises the devices that own
- * them).  Returns FA_OK or FA_ERR_HIP. */
+/* Frees the internal workspaces of fa_decode, fa_decode_paged and fa_bwd
+ * (synchronises the devices that own them).  Returns FA_OK or FA_ERR_HIP. */
 int fa_release_workspace(void);
 
 /* Static description of a status code, and the thread-local message of the

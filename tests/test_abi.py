@@ -252,3 +252,46 @@ def test_decode_paged_split_count():
     assert fa.fa_decode_paged_splits(1, 32, 100000, 16, 8) == 0
     assert fa.fa_decode_paged_splits(1, 32, 64, 12, 8) == 0
     assert fa.fa_decode_paged_splits(2, 4, 64, 16, 5) == 5
+
+
+def _bwd(Q=A, K=2 * A, V=3 * A, O=4 * A, dO=5 * A, L=6 * A, dQ=7 * A, dK=8 * A, dV=9 * A, B=1, H=1, N=16, d=64,
+         causal=0, scale=0.125, ws=None, ws_bytes=0):
+    lib = _fa().lib
+    return lib.fa_bwd(Q, K, V, O, dO, L, dQ, dK, dV, B, H, N, d, causal, ctypes.c_float(scale), ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize(
+    "kw,status,msg",
+    [
+        (dict(Q=None), -1, "null"),
+        (dict(dO=None), -1, "null"),
+        (dict(L=None), -1, "null"),
+        (dict(dV=None), -1, "null"),
+        (dict(B=0), -1, ">= 1"),
+        (dict(N=0), -1, ">= 1"),
+        (dict(d=96), -2, "not supported"),
+        (dict(causal=3), -1, "causal"),
+        (dict(scale=float("nan")), -1, "scale"),
+        (dict(dK=8 * A + 8), -1, "aligned"),
+        (dict(L=6 * A + 2), -1, "aligned"),
+        (dict(dQ=A + 256), -1, "overlap an input"),
+        (dict(dV=6 * A), -1, "overlap L"),
+        (dict(dK=7 * A + 1024), -1, "each other"),
+        (dict(ws=10 * A + 64, ws_bytes=1 << 20), -5, "aligned"),
+        (dict(ws=10 * A, ws_bytes=16), -5, "too small"),
+        (dict(ws=None, ws_bytes=16), -5, "nonzero"),
+        (dict(ws=9 * A, ws_bytes=1 << 20), -1, "overlaps"),
+    ],
+)
+def test_bwd_rejects_invalid_arguments(kw, status, msg):
+    """Every argument is checked on the host before any HIP call."""
+    fa = _fa()
+    assert _bwd(**kw) == status
+    assert msg in fa.last_error()
+
+
+def test_bwd_workspace_formula():
+    fa = _fa()
+    for B, H, N in ((1, 1, 1), (2, 3, 100), (1, 32, 8192)):
+        assert fa.fa_bwd_workspace_bytes(B, H, N) == -(-(B * H * N * 4) // 256) * 256
+    assert fa.fa_bwd_workspace_bytes(0, 1, 1) == 0
