@@ -24,7 +24,8 @@ __host__ __device__ constexpr int fwd_lds_bytes(int d) { return 4 * kFwdBC * (2 
 constexpr int kF32BR = 64;
 constexpr int kF32BC = 64;
 
-// bf16 backward: wavefronts per workgroup (one per SIMD); the dK/dV kernel
+// bf16 backward: wavefronts per workgroup (two workgroups per compute unit,
+// so two wavefronts per SIMD); the dK/dV kernel
 // gives each wavefront 32 keys (kBwdKV per workgroup) and walks query tiles
 // of kBwdQT rows; the dQ kernel gives each wavefront 32 queries (kBwdQ per
 // workgroup) and walks KV tiles of kBwdKT keys.  LDS: two buffers of
@@ -32,11 +33,12 @@ constexpr int kF32BC = 64;
 // padded by 16 bytes.
 constexpr int kBwdWaves = 4;
 constexpr int kBwdKV = 32 * kBwdWaves;
-constexpr int kBwdQT = 64;
+constexpr int kBwdQT = 32;
 constexpr int kBwdQ = 32 * kBwdWaves;
 constexpr int kBwdKT = 64;
-__host__ __device__ constexpr int bwd_dkdv_lds_bytes(int d) { return 2 * (2 * kBwdQT * (2 * d + 16) + 2 * 1024); }
-__host__ __device__ constexpr int bwd_dq_lds_bytes(int d) { return 2 * 2 * kBwdKT * (2 * d + 16); }
+__host__ __device__ constexpr int bwd_tile_bytes(int rows, int d) { return (rows * (2 * d + 16) + 1023) / 1024 * 1024; }
+__host__ __device__ constexpr int bwd_dkdv_lds_bytes(int d) { return 2 * (2 * bwd_tile_bytes(kBwdQT, d) + 2 * 1024); }
+__host__ __device__ constexpr int bwd_dq_lds_bytes(int d) { return 2 * 2 * bwd_tile_bytes(kBwdKT, d); }
 
 // Decode split kernel: wavefronts per workgroup; chunk lengths are rounded up
 // to a multiple of kDecChunkAlign tokens.
