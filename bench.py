@@ -14,8 +14,9 @@ bracketed by HIP events on the stream it is launched on.
 Printed: one JSON line.  `value` is fa_fwd TFLOP/s on prefill_8k (algorithmic
 4*B*H*N^2*d FLOPs over the measured kernel time); decode GB/s (algorithmic
 K+V bytes over split+combine time) is reported beside it, together with the
-roofline fractions, the extra workloads (causal_4k, decode_varlen) and the
-float64 oracle timed on a bounded sample on the host cores.
+roofline fractions, the extra workloads (causal_4k, decode_varlen, and the
+backward fa_bwd on prefill_8k and causal_4k) and the float64 oracle timed on
+a bounded sample on the host cores.
 """
 
 import argparse
@@ -302,6 +303,33 @@ def main():
         }
         del qv, Kv, Vv, ov
         log(f"decode_varlen {ms_v * 1e3:.1f} us -> {gbs_v:.1f} GB/s")
+
+    # ---------------- the backward (gradients by recomputation from O and L)
+    if not args.no_extra:
+        result["backward"] = {}
+        for name in ("prefill_8k", "causal_4k"):
+            bc = synth.WORKLOADS[name]
+            Bb, Hb, Nb, db_ = bc["B"], bc["H"], bc["N"], bc["d"]
+            Qb, Kb, Vb = (Q, K, V) if name == "prefill_8k" else synth.prefill_inputs(name, dev)
+            dOb = synth.torch_normal(850, (Bb, Hb, Nb, db_), dev, "bf16")
+            Ob = torch.empty_like(Qb)
+            Lb = torch.empty(Bb, Hb, Nb, device=dev)
+            fa.fa_fwd(Qb, Kb, Vb, Ob, Lb, causal=bc["causal"])
+            gq, gk, gv = (torch.empty_like(Qb) for _ in range(3))
+            ms_b = _timed(lambda i: fa.fa_bwd(Qb, Kb, Vb, Ob, dOb, Lb, gq, gk, gv, causal=bc["causal"]), K_, W_, torch)
+            pairs = Nb * (Nb + 1) / 2 if bc["causal"] else Nb * Nb
+            alg = 10.0 * db_ * Bb * Hb * pairs
+            result["backward"][name] = {
+                "value": round(alg / (ms_b * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "ms_per_launch": round(ms_b, 4),
+                "frac_of_peak": round(alg / (ms_b * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                "flops_algorithmic": alg, "flops_executed": 1.4 * alg,
+                "note": "10 N^2 d per head (the lecture notes' count with recomputation; causal: unmasked pairs); "
+                        "the kernels execute 14 N^2 d (dQ recomputes S and dP)",
+            }
+            log(f"backward {name} {ms_b:.3f} ms -> {result['backward'][name]['value']} TFLOP/s")
+            del Ob, Lb, gq, gk, gv, dOb
+            if name != "prefill_8k":
+                del Qb, Kb, Vb
 
     # ---------------- light parity check of the timed outputs
     q0, Kc0, Vc0, _ = caches[(K_ - 1) % n_rot]
