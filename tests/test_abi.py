@@ -73,6 +73,7 @@ def _fwd(fn, Q=A, K=2 * A, V=3 * A, O=4 * A, L=None, B=1, H=1, N=16, d=64, causa
         (dict(O=2 * A + 64), -1, "overlaps"),
         (dict(L=4 * A + 8), -1, "overlaps"),
         (dict(L=5 * A + 2), -1, "aligned"),
+        (dict(N=1 << 24, d=128), -1, "2 GiB"),
     ],
 )
 def test_fwd_rejects_invalid_arguments(fn, kw, status, msg):
@@ -281,6 +282,8 @@ def _bwd(Q=A, K=2 * A, V=3 * A, O=4 * A, dO=5 * A, L=6 * A, dQ=7 * A, dK=8 * A, 
         (dict(ws=10 * A, ws_bytes=16), -5, "too small"),
         (dict(ws=None, ws_bytes=16), -5, "nonzero"),
         (dict(ws=9 * A, ws_bytes=1 << 20), -1, "overlaps"),
+        (dict(N=1 << 24, d=128), -1, "2 GiB"),
+        (dict(B=1 << 16, H=1 << 16, N=64), -1, "grid too large"),
     ],
 )
 def test_bwd_rejects_invalid_arguments(kw, status, msg):

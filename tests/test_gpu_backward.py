@@ -137,3 +137,15 @@ def test_bwd_workload_shapes(name):
     worst = _compare(Q, K, V, dO, dQ, dK, dV, causal, 1 / math.sqrt(cfg["d"]), heads=[(0, 0), (B - 1, H - 1)])
     print(f"{name} {worst}")
     assert max(worst.values()) <= 1.0, worst
+
+
+def test_bwd_long_sequence_one_head():
+    """N = 16384 non-causal and causal, one head compared in full."""
+    _say("bwd N=16384")
+    shape = (1, 1, 16384, 128)
+    Q, K, V, dO = (synth.torch_normal(860 + t, shape, "cuda", "bf16") for t in range(4))
+    for causal in (False, True):
+        _, _, dQ, dK, dV = _run(Q, K, V, dO, causal)
+        worst = _compare(Q, K, V, dO, dQ, dK, dV, causal, 1 / math.sqrt(128))
+        print(f"N=16384 causal={causal} {worst}")
+        assert max(worst.values()) <= 1.0, (causal, worst)

@@ -394,3 +394,61 @@ def test_decode_varlen_workload_sampled():
     print(f"decode_varlen sampled max|dO|={dO:.3e} max|dL|={dL:.3e}")
     assert dO <= BF16_O and dL <= BF16_L
     assert torch.isfinite(o.float()).all()
+
+
+# --------------------------------------------------------------------------
+# larger than the workloads: long sequences, many heads, long caches
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bf16_long_sequence_sampled(causal):
+    """N = 65536 (256 query tiles, 1024 KV tiles per head), sampled rows."""
+    fa = _fa()
+    _say("bf16 N=65536", causal)
+    shape = (1, 2, 65536, 128)
+    Q, K, V = (synth.torch_normal(900 + t, shape, "cuda", "bf16") for t in range(3))
+    O = torch.empty_like(Q)
+    L = torch.empty(shape[:3], device="cuda")
+    fa.fa_fwd(Q, K, V, O, L, causal=causal)
+    torch.cuda.synchronize()
+    rows = _rows_sample(shape[2], 3)
+    dO, dL = _prefill_compare(Q, K, V, O, L, 1 / math.sqrt(128), causal, rows=rows, heads=[(0, 0), (0, 1)])
+    print(f"N=65536 causal={causal} max|dO|={dO:.3e} max|dL|={dL:.3e}")
+    assert dO <= BF16_O and dL <= BF16_L
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bf16_many_heads_sampled(causal):
+    """B = 16, H = 128: 2048 heads, several units per persistent workgroup
+    (causal) or eight query tiles per head spread over the XCDs."""
+    fa = _fa()
+    _say("bf16 2048 heads", causal)
+    shape = (16, 128, 1000, 64)
+    Q, K, V = (synth.torch_normal(910 + t, shape, "cuda", "bf16") for t in range(3))
+    O = torch.empty_like(Q)
+    L = torch.empty(shape[:3], device="cuda")
+    fa.fa_fwd(Q, K, V, O, L, causal=causal)
+    torch.cuda.synchronize()
+    heads = [(0, 0), (3, 77), (9, 1), (15, 127)]
+    dO, dL = _prefill_compare(Q, K, V, O, L, 1 / math.sqrt(64), causal, heads=heads)
+    assert dO <= BF16_O and dL <= BF16_L
+    assert torch.isfinite(O).all() and torch.isfinite(L).all()
+
+
+@pytest.mark.parametrize("splits", [0, 256])
+def test_decode_million_token_cache(splits):
+    """One query against 2^20 cached keys per head."""
+    fa = _fa()
+    _say("decode L=2^20", splits)
+    B, H, Lc, d = 1, 2, 1 << 20, 128
+    q = synth.torch_normal(920, (B, H, d), "cuda")
+    Kc = synth.torch_normal(921, (B, H, Lc, d), "cuda")
+    Vc = synth.torch_normal(922, (B, H, Lc, d), "cuda")
+    lengths = np.array([Lc], dtype=np.int64)
+    Lkv = torch.tensor(lengths, dtype=torch.int32, device="cuda")
+    o = torch.empty_like(q)
+    fa.fa_decode(q, Kc, Vc, o, Lkv, num_splits=splits)
+    torch.cuda.synchronize()
+    dO, _ = _decode_compare(q, Kc, Vc, o, lengths)
+    print(f"decode L=2^20 splits={splits} max|dO|={dO:.3e}")
+    assert dO <= BF16_O
