@@ -17,7 +17,10 @@
 //    SIMD (wavefronts w and w+4 share a SIMD).
 //  * Q is read once, straight from HBM into registers, already in the
 //    operand layout of the score product; LDS holds only K and V tiles
-//    (double-buffered, kFwdBC keys each).
+//    (double-buffered, kFwdBC keys each).  At the end of a query tile the
+//    output rows pass through the then idle K/V area, so that they leave as
+//    whole rows (16 lanes per 256-byte row) rather than as 32 row pieces per
+//    store instruction.
 //  * Scores are formed transposed, S^T = K_j Q_i^T, on
 //    v_mfma_f32_32x32x16_bf16.  In the 32x32 accumulator layout a lane holds
 //    one query column and 16 key rows per 32-key block, so the softmax
@@ -153,9 +156,9 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ K
     return n;
   };
 
-  // ---- start of an item (query tile qt of head bh): Q into registers and
+  // ---- start of an item (query tile qt of head bh): Q into registers, and
   // K_0, V_0, K_1 into LDS.  Only issues loads; the item waits for them.
-  auto start_item = [&](const int bh, const int qt) {
+  auto start_q = [&](const int bh, const int qt) {
     const size_t head_off = (size_t)bh * N * D;
     const int qrow = qt * kFwdBR + wave * 32 + l32;
     // rows past N read as zeros; their outputs are never stored
@@ -166,6 +169,9 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ K
 #pragma unroll
       for (int ds = 0; ds < D / 16; ++ds) qf[ds] = qp[2 * ds];
     }
+  };
+  auto start_kv = [&](const int bh, const int qt) {
+    const size_t head_off = (size_t)bh * N * D;
     const u32x4_t k_rsrc = make_rsrc(Kg + head_off, head_bytes);
     const u32x4_t v_rsrc = make_rsrc(Vg + head_off, head_bytes);
     dma_tile(k_rsrc, k_voff, 0, kbuf(0));
@@ -243,8 +249,8 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ K
     wg_barrier();
   };
 
-  // ---- slot 0: the loads of start_item have landed (and the stores of the
-  // previous item's O are complete), S_0 everywhere
+  // ---- slot 0: the loads of start_q and start_kv have landed (and the
+  // stores of the previous item's O are complete), S_0 everywhere
   wait_vmem();
   __syncthreads();
   f32x16_t s[kKB];  // scores of the current tile
@@ -348,29 +354,56 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ K
   wg_barrier();
   };
 
-  // ---- end of an item: O = U / l, L = m * scale + ln l
+  // ---- end of an item: O = U / l, L = m * scale + ln l.  Called after
+  // the item's last barrier, when no wavefront reads the K/V tiles any more:
+  // O goes through the wavefront's own 32 padded rows of that area, in
+  // which each lane writes its row's pieces; whole rows then leave with one
+  // 16-byte store per lane, D/8 lanes per row.  (Stored straight from the
+  // accumulator layout, every store instruction would touch 32 rows.)
   auto finish_item = [&](const int bh, const int qt) {
   const size_t head_off = (size_t)bh * N * D;
-  const int qrow = qt * kFwdBR + wave * 32 + l32;
+  const int qw0 = qt * kFwdBR + wave * 32;
+  const int qrow = qw0 + l32;
   const float l_tot = pair_sum(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  if (qrow < N) {
-    __bf16* orow = Og + head_off + (size_t)qrow * D;
+  char LDS_AS* const stage = lds + wave * 32 * T::kStride;
+  // the lane index as an opaque copy, so that the lane-dependent addresses
+  // below are formed here and not hoisted out of the item loop, where they
+  // would hold registers across the tile loop
+  int ln = lane;
+  asm volatile("" : "+v"(ln));
+  {
+    // lane (l32, g) holds head dimensions db*32 + 8*i4 + 4*g + 0..3
+    char LDS_AS* ob = stage + (ln & 31) * T::kStride + 8 * (ln >> 5);
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
-        const int d0 = db * 32 + 8 * i4 + 4 * g;
         u32x2_t v;
         v[0] = pack_bf16x2(u[db][4 * i4 + 0] * inv, u[db][4 * i4 + 1] * inv);
         v[1] = pack_bf16x2(u[db][4 * i4 + 2] * inv, u[db][4 * i4 + 3] * inv);
-        *reinterpret_cast<u32x2_t*>(orow + d0) = v;
+        *(u32x2_t LDS_AS*)(ob + 64 * db + 16 * i4) = v;
       }
     }
-    if (Lg != nullptr && g == 0) {
-      Lg[(size_t)bh * N + qrow] = l_tot > 0.f ? m_ref * scale + __logf(l_tot) : -INFINITY;
+  }
+  // the rows are this wavefront's own, and LDS serves a wavefront in order
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  {
+    constexpr int kRowsPer = 64 / T::kChunks;  // rows per store instruction
+    const int rr = ln / T::kChunks, ch = ln % T::kChunks;
+#pragma unroll
+    for (int k = 0; k < 32 / kRowsPer; ++k) {
+      const int r = k * kRowsPer + rr;
+      const u32x4_t v = *(const u32x4_t LDS_AS*)(stage + r * T::kStride + ch * 16);
+      if (qw0 + r < N) *reinterpret_cast<u32x4_t*>(Og + head_off + (size_t)(qw0 + r) * D + ch * 8) = v;
     }
   }
+  if (Lg != nullptr && g == 0 && qrow < N) {
+    Lg[(size_t)bh * N + qrow] = l_tot > 0.f ? m_ref * scale + __logf(l_tot) : -INFINITY;
+  }
+  // every wavefront has read its O rows back before K/V loads reuse the area
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  wg_barrier();
   };
 
   // ---- workgroup -> work units.  A unit is one query tile, or for causal
@@ -389,7 +422,8 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ K
   const int logical = xcd * per + (xcd < rem ? xcd : rem) + slot_id;
   if constexpr (CAUSAL) {
     // items in order: per unit the longer query tile, then the shorter one;
-    // the next item's loads are issued before this item's O is stored
+    // the next item's Q loads are issued before this item's O is stored, its
+    // K/V loads after (O passes through the K/V area)
     const int pairs_per_head = (q_tiles + 1) >> 1;
     int unit = logical, second = 0;
     auto item_of = [&](int un, int sec, int& bh, int& qt) {
@@ -399,7 +433,8 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ K
     };
     int bh, qt;
     item_of(unit, second, bh, qt);
-    start_item(bh, qt);
+    start_q(bh, qt);
+    start_kv(bh, qt);
     for (;;) {
       run_item(bh, qt);
       // advance: the shorter tile of this pair if it is distinct, else the
@@ -415,10 +450,11 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ K
       int nbh = 0, nqt = 0;
       if (more) {
         item_of(unit, second, nbh, nqt);
-        start_item(nbh, nqt);
+        start_q(nbh, nqt);
       }
       finish_item(bh, qt);
       if (!more) break;
+      start_kv(nbh, nqt);
       bh = nbh;
       qt = nqt;
     }
@@ -426,7 +462,8 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ K
     // one workgroup per query tile (the grid equals the unit count)
     const int bh = logical / q_tiles;
     const int qt = logical - bh * q_tiles;
-    start_item(bh, qt);
+    start_q(bh, qt);
+    start_kv(bh, qt);
     run_item(bh, qt);
     finish_item(bh, qt);
   }
