@@ -73,6 +73,31 @@ constexpr int kKS = kFwdBC / 16;  // 16-key MFMA steps per KV tile
 #define FA_FWD_PINGPONG 1  // 0: every wavefront in group 0 (lockstep slots)
 #endif
 
+// Issue order of the matrix slot's kR LDS reads (the transposing V reads,
+// then the K-fragment reads) among its kM MFMAs: kUp = kR/4 reads first,
+// then after MFMA i enough reads that kUp + (i+1)(kR - kUp)/kSpan have been
+// issued, so the last read goes out after MFMA kSpan-1, kSpan = 5 kM / 8
+// (12 and 20 of 48 reads and 32 MFMAs at d = 128; measured flat from 10 to
+// 14 and from 16 to 22).  Left to itself the compiler issues the K reads of
+// the next scores only after the last W.V product and then keeps two in
+// flight, so the scores wait on LDS latency.
+template <int I, int kM, int kR>
+__device__ __forceinline__ void pin_matrix_steps() {
+  constexpr int kUp = kR / 4, kSpan = 5 * kM / 8;
+  if constexpr (I < kM) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+    constexpr int before = I < kSpan ? kUp + I * (kR - kUp) / kSpan : kR;
+    constexpr int after = I + 1 < kSpan ? kUp + (I + 1) * (kR - kUp) / kSpan : kR;
+    if constexpr (after > before) __builtin_amdgcn_sched_group_barrier(0x100, after - before, 0);  // LDS reads
+    pin_matrix_steps<I + 1, kM, kR>();
+  }
+}
+template <int kM, int kR>
+__device__ __forceinline__ void pin_matrix_slot() {
+  __builtin_amdgcn_sched_group_barrier(0x100, kR / 4, 0);
+  pin_matrix_steps<0, kM, kR>();
+}
+
 template <int D>
 struct Tile {
   static constexpr int kRowBytes = D * 2;
@@ -318,12 +343,13 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ K
     keep(l_run);
     end_slot(sa);
 
-    // -- matrix slot of tile j (MFMA): U^T += V_j^T W^T (a wavefront with
-    // every row before this tile's first key has only zero weights: skip
-    // it), then the scores of tile j+1
+    // -- matrix slot of tile j (MFMA): U^T += V_j^T W^T, then the scores of
+    // tile j+1, as one straight-line block whose read/MFMA interleave is
+    // pinned.  Both run unconditionally: a wavefront whose rows all precede
+    // this tile's first key has W = 0 and adds exact zeros, and after the
+    // last tile the scores of a stale K buffer are formed and never used.
     issue_slot(sa + 1);
-    const bool wave_live = !CAUSAL || (j * kFwdBC <= qw0 + 31);
-    if (wave_live) {
+    {
       const char LDS_AS* vb = vbuf(j & 1) + v_base;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) {
@@ -334,10 +360,9 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ K
         }
       }
     }
-    if (j + 1 < n_tiles) {
-      scores(kbuf((j + 1) & 1), s);
-      if (needs_mask(j + 1)) apply_mask(j + 1, s);
-    }
+    scores(kbuf((j + 1) & 1), s);
+    pin_matrix_slot<2 * (D / 32) * kKS, 2 * (D / 32) * kKS + (D / 16) * kKB>();
+    if (j + 1 < n_tiles && needs_mask(j + 1)) apply_mask(j + 1, s);
     // keep the products in this slot
 #pragma unroll
     for (int cb = 0; cb < kKB; ++cb) keep(s[cb]);
