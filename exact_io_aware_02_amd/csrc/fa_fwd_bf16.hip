@@ -37,11 +37,13 @@
 //    loop (16-byte K fragments, transposing V reads) is free of bank
 //    conflicts and addressed by one per-lane base register plus a
 //    compile-time offset.
-//  * Ping-pong schedule: each KV tile takes two barrier-separated slots per
-//    wavefront, a softmax slot (VALU only) and a matrix slot (MFMA only: the
-//    W V product of this tile, then the scores of the next).  The two
-//    wavefronts of a SIMD run one slot apart, so the matrix core works on one
-//    wavefront's products while the other computes its exponentials.
+//  * Ping-pong schedule: each KV tile takes two slots per wavefront, a
+//    softmax slot (VALU only) and a matrix slot (MFMA only: the W V product
+//    of this tile, then the scores of the next).  The two wavefronts of a
+//    SIMD run one slot apart, so the matrix core works on one wavefront's
+//    products while the other computes its exponentials; a workgroup barrier
+//    after every second slot (the one that also guards the K/V buffers)
+//    keeps them in step.
 //  * U^T lives in the accumulator layout with the query on the lane, so a
 //    rescale by alpha is one multiply per register.  Rescaling is
 //    conditional ("Infra: Flash Attention", section "Invariant of
@@ -251,8 +253,8 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ K
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) u[db] = f32x16_t{};
 
-  // ---- slot schedule.  The loop runs in slots separated by workgroup
-  // barriers.  Each KV tile j takes two slots per wavefront: a softmax slot
+  // ---- slot schedule.  The loop runs in slots; a workgroup barrier ends
+  // every odd slot.  Each KV tile j takes two slots per wavefront: a softmax slot
   // (VALU only: W = exp2(c S_j - c m), l, rescale) and a matrix slot (MFMA
   // only: U^T += V_j^T W^T, then S_{j+1} = K_{j+1} Q^T).  Group 0 (waves
   // 0-3) runs tile j in slots 2j+1, 2j+2; group 1 (waves 4-7, the other
@@ -261,7 +263,9 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ K
   // Slot 0 forms S_0 everywhere; group 1 idles in slot 1.  Loads are issued
   // in even slots 2t (t >= 1): K_{t+1} and V_t, each into the buffer whose
   // last reader ran in slot 2t-1; they are waited for at the end of slot
-  // 2t+1, before their first reader in slot 2t+2.
+  // 2t+1, before their first reader in slot 2t+2.  Those are the only
+  // orderings the buffers need, so only odd slots end with a barrier (with
+  // one after every slot, causal and non-causal prefill were 1-2 % slower).
   auto issue_slot = [&](int s) {
     if ((s & 1) == 0 && s >= 2) {
       const int t = s >> 1;
@@ -270,8 +274,10 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ K
     }
   };
   auto end_slot = [&](int s) {
-    if (s & 1) wait_vmem();
-    wg_barrier();
+    if (s & 1) {
+      wait_vmem();
+      wg_barrier();
+    }
   };
 
   // ---- slot 0: the loads of start_q and start_kv have landed (and the
@@ -368,9 +374,9 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ K
     for (int cb = 0; cb < kKB; ++cb) keep(s[cb]);
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) keep(u[db]);
-    // every wavefront passes 2 * n_tiles + 1 barriers in the loop and slot
-    // 0: group 1 has the extra idle slot 1, so it skips the barrier after
-    // its final slot
+    // every wavefront passes n_tiles barriers in the loop (odd slots 1, 3,
+    // ..., 2 n_tiles - 1): group 1 has the extra idle slot 1, so it skips
+    // the end of its final slot 2 n_tiles + 1
     if (!(grp == 1 && j == n_tiles - 1)) end_slot(sa + 1);
   }
 
