@@ -21,12 +21,17 @@ INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libfa.so")
 
-SOURCES = ["fa_api.hip", "fa_fwd_bf16.hip", "fa_fwd_f32.hip", "fa_decode.hip", "fa_bwd_bf16.hip"]
+SOURCES = ["fa_api.hip", "fa_fwd_bf16.hip", "fa_fwd_bf16_asm.hip", "fa_fwd_f32.hip", "fa_decode.hip",
+           "fa_bwd_bf16.hip"]
+# generated before compiling: the assembly of the 64-rows-per-wavefront
+# forward's tile loop (fa_fwd_bf16_asm.hip includes it)
+GENERATED = os.path.join(CSRC, "fa_fwd_asm_d128.inc")
 # NaN inputs are outside the contract of the bf16 kernels; without NaN
 # semantics fmaxf needs no canonicalisation and fuses into v_max3_f32.
 # Infinities stay honoured (masked scores are -inf).
 PER_SOURCE_FLAGS = {
     "fa_fwd_bf16.hip": ["-fno-honor-nans"],
+    "fa_fwd_bf16_asm.hip": ["-fno-honor-nans"],
     "fa_decode.hip": ["-fno-honor-nans"],
     "fa_bwd_bf16.hip": ["-fno-honor-nans"],
 }
@@ -69,6 +74,7 @@ def build(verbose=False, resource_usage=False):
     """Compile every source and link libfa.so; returns its path."""
     os.makedirs(OBJDIR, exist_ok=True)
     hipcc = _hipcc()
+    _run([sys.executable, os.path.join(PKG, "gen_fwd_asm.py"), GENERATED], verbose)
     extra = ["-Rpass-analysis=kernel-resource-usage"] if resource_usage else []
     objs = []
     cmds = []

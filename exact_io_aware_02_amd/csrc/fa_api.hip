@@ -289,7 +289,7 @@ int fa_fwd_plan(int B, int H, int N, int d, int causal, fa_fwd_plan_t* out) {
   out->block_cols = fa::kFwdBC;
   out->q_tiles = q_tiles;
   out->kv_tiles = (int)fa::ceil_div64(N, fa::kFwdBC);
-  out->threads_per_workgroup = fa::kFwdWaves * 64;
+  out->threads_per_workgroup = fa::fwd_threads(d, causal);
   out->lds_bytes = fa::fwd_lds_bytes(d);
   out->work_units = fa::fwd_units(B, H, N, causal);
   out->workgroups = fa::fwd_grid(out->work_units, causal, kPlanCUs);

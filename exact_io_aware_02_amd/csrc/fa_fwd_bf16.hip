@@ -514,7 +514,8 @@ hipError_t launch(const FwdArgs& a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, int d, hipStream_t stream) {
-  if (d == 128) return a.causal ? launch<128, true>(a, stream) : launch<128, false>(a, stream);
+  if (fwd_uses_asm(d, a.causal)) return launch_fwd_bf16_asm(a, stream);
+  if (d == 128) return launch<128, true>(a, stream);  // non-causal d = 128 runs the other kernel
   return a.causal ? launch<64, true>(a, stream) : launch<64, false>(a, stream);
 }
 

@@ -1,0 +1,147 @@
+// FlashAttention forward for bf16 Q/K/V, d = 128, no causal mask, on gfx950:
+// 64 query rows per wavefront, one wavefront per SIMD, the tile loop in
+// generated assembly.
+//
+// Same computation as fa_fwd_bf16.hip: Algorithm 1 of "Infra: Flash
+// Attention" (section "Tiled computation and forward") in the
+// FlashAttention-2 order of the "CMU 10-423 Lecture 18" notes (section 3.4),
+// with conditional rescaling ("Invariant of conditional rescaling").  What
+// differs is the split of the work on a compute unit:
+//  * 4 wavefronts of 64 query rows (B_r = 256), one per SIMD.  Every K or V
+//    fragment read from LDS feeds two 32-query MFMAs, so a KV tile costs half
+//    the LDS reads per flop of the 32-rows-per-wavefront kernel.
+//  * Inside a wavefront, tile step j overlaps U += V_{j-1}^T W_{j-1}^T and
+//    S_{j+1} = K_{j+1} Q^T on the matrix core with the softmax of S_j on the
+//    VALU (the FlashAttention-3 overlap of the blog's FA-3 section).  A
+//    wavefront keeps issuing independent VALU work while its MFMAs run.
+//  * The softmax of a tile forms no row max while the base holds: weights
+//    relative to the current base are summed, and only a tile whose sum
+//    exceeds 2^8 (so possibly a weight above the threshold) is redone with
+//    its row max and a rescale of U and l.
+//  * U^T (128 registers) and the Q fragments (64) live in AGPRs, two score
+//    and two probability tiles in VGPRs.  The compiler cannot hold that many
+//    values without spilling, so one query tile's loop is assembly generated
+//    by gen_fwd_asm.py with one fixed register for every value.
+
+#include "fa_device.h"
+#include "fa_internal.h"
+#include "fa_fwd_asm_d128.inc"
+
+namespace fa {
+namespace {
+
+using namespace dev;
+
+constexpr int D = 128;
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * 64;
+constexpr int kBR = 64 * kWaves;
+constexpr int kBC = 64;
+constexpr int kStride = 2 * D + 16;
+constexpr int kTile = kBC * kStride;
+constexpr int kLds = 4 * kTile;
+static_assert(kBR == kFwdBR && kBC == kFwdBC, "tiles must match the planner");
+static_assert(kLds == fwd_lds_bytes(D), "LDS size must match the planner");
+
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void fwd_bf16_asm_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ Kg,
+                         const __bf16* __restrict__ Vg, __bf16* __restrict__ Og,
+                         float* __restrict__ Lg, int N, int q_tiles, float scale) {
+  __shared__ __attribute__((aligned(1024))) char smem[kLds];
+  char LDS_AS* lds = (char LDS_AS*)smem;
+  const unsigned lds_base = (unsigned)(size_t)lds;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31;
+  const int g = lane >> 5;
+
+  // per-lane buffer->LDS source offsets of this wavefront's 1 KiB blocks
+  unsigned kvo[5], vvo[5];
+#pragma unroll
+  for (int p = 0; p < 5; ++p) {
+    const int o = (wave + p * kWaves) * 1024 + lane * 16;
+    kvo[p] = padded_source<D>(o, false);
+    vvo[p] = padded_source<D>(o, true);
+  }
+  // LDS read bases: K fragments, transposing V reads (V buffers start after
+  // the two K buffers), this wavefront's 64 output staging rows
+  const unsigned kb = lds_base + l32 * kStride + g * 16;
+  const unsigned vb = lds_base + 2 * kTile + tr_lane_base<kStride>(lane);
+  const unsigned stg = lds_base + wave * 64 * kStride + l32 * kStride + 8 * g;
+  const unsigned wbase = lds_base + wave * 1024;
+
+  const float c = scale * kLog2e;
+  const float theta = 8.f / c;  // conditional-rescale threshold, raw score units
+  const unsigned head_bytes = (unsigned)N * D * 2;
+
+
+  // one query tile: the generated loop, then O and L of this wavefront's rows
+  auto item = [&](const int bh, const int qt) {
+    const size_t head_off = (size_t)bh * N * D;
+    const int qw0 = __builtin_amdgcn_readfirstlane(qt * kBR + wave * 64);
+    const int n = (N + kBC - 1) / kBC;
+    const u32x4_t q_rsrc = make_rsrc(Qg + head_off, head_bytes);
+    const u32x4_t k_rsrc = make_rsrc(Kg + head_off, head_bytes);
+    const u32x4_t v_rsrc = make_rsrc(Vg + head_off, head_bytes);
+    const unsigned qvo = (unsigned)(qw0 + l32) * D * 2 + g * 16;
+    // keys past N are masked: the loop compares key - 4 g against N - 1 - 4 g
+    const int limg = N - 1 - 4 * g;
+    float mo0, mo1, lo0, lo1;
+    asm volatile(FA_ASM_ITEM
+                 : [mo0] "=v"(mo0), [mo1] "=v"(mo1), [lo0] "=v"(lo0), [lo1] "=v"(lo1)
+                 : [kvo0] "v"(kvo[0]), [kvo1] "v"(kvo[1]), [kvo2] "v"(kvo[2]), [kvo3] "v"(kvo[3]),
+                   [kvo4] "v"(kvo[4]), [vvo0] "v"(vvo[0]), [vvo1] "v"(vvo[1]), [vvo2] "v"(vvo[2]),
+                   [vvo3] "v"(vvo[3]), [vvo4] "v"(vvo[4]), [qvo] "v"(qvo), [kb] "v"(kb), [vb] "v"(vb),
+                   [stg] "v"(stg), [limg0] "v"(limg), [limg1] "v"(limg), [qrsrc] "s"(q_rsrc),
+                   [krsrc] "s"(k_rsrc), [vrsrc] "s"(v_rsrc), [n] "s"(n), [c] "v"(c), [theta] "v"(theta),
+                   [wave] "s"(wave), [wbase] "s"(wbase), [n_keys] "s"(N), [qw0] "s"(qw0)
+                 : FA_ASM_CLOBBERS);
+    // the wavefront's 64 rows of O wait in its staging rows (written and
+    // waited for by the loop): whole rows leave with one 16-byte store per
+    // lane, 16 lanes per 256-byte row
+    const char LDS_AS* stage = lds + wave * 64 * kStride;
+    const int rr = lane >> 4, ch = lane & 15;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int r = 4 * k + rr;
+      const u32x4_t v = *(const u32x4_t LDS_AS*)(stage + r * kStride + ch * 16);
+      if (qw0 + r < N) *reinterpret_cast<u32x4_t*>(Og + head_off + (size_t)(qw0 + r) * D + ch * 8) = v;
+    }
+    if (Lg != nullptr && g == 0) {
+      if (qw0 + l32 < N) Lg[(size_t)bh * N + qw0 + l32] = mo0 * scale + __logf(lo0);
+      if (qw0 + 32 + l32 < N) Lg[(size_t)bh * N + qw0 + 32 + l32] = mo1 * scale + __logf(lo1);
+    }
+    // every wavefront has read its rows back before the next item's loads
+    // reuse the area
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    wg_barrier();
+  };
+
+  // one workgroup per query tile; workgroup ids are remapped so that the
+  // query tiles running at once on an XCD (dispatch is round-robin over the 8
+  // XCDs) belong to the same heads and share their K/V in that XCD's L2
+  const int G = gridDim.x;
+  const int wg = blockIdx.x;
+  const int per = G >> 3, rem = G & 7;
+  const int xcd = wg & 7, slot_id = wg >> 3;
+  const int logical = xcd * per + (xcd < rem ? xcd : rem) + slot_id;
+  const int bh = logical / q_tiles;
+  item(bh, logical - bh * q_tiles);
+}
+
+hipError_t launch(const FwdArgs& a, hipStream_t stream) {
+  const int q_tiles = (a.N + kBR - 1) / kBR;
+  hipLaunchKernelGGL(fwd_bf16_asm_kernel, dim3((unsigned)a.grid), dim3(kThreads), 0, stream,
+                     static_cast<const __bf16*>(a.Q), static_cast<const __bf16*>(a.K),
+                     static_cast<const __bf16*>(a.V), static_cast<__bf16*>(a.O), a.L, a.N, q_tiles,
+                     a.scale);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fwd_bf16_asm(const FwdArgs& a, hipStream_t stream) { return launch(a, stream); }
+
+}  // namespace fa

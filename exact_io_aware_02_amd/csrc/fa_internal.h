@@ -96,8 +96,16 @@ struct DecodeArgs {
   int max_blocks = 0, log2_bs = 0, num_blocks = 0;
 };
 
+// bf16 prefill with d = 128 and no causal mask runs the 64-rows-per-wavefront
+// kernel (4 wavefronts of 64 query rows, tile loop in generated assembly);
+// every other bf16 prefill the 32-rows-per-wavefront one (8 wavefronts).
+// Both use the tiles above.
+inline bool fwd_uses_asm(int d, int causal) { return d == 128 && !causal; }
+inline int fwd_threads(int d, int causal) { return fwd_uses_asm(d, causal) ? 4 * 64 : kFwdWaves * 64; }
+
 // Launchers: enqueue on `stream`, return hipGetLastError().
 hipError_t launch_fwd_bf16(const FwdArgs& a, int d, hipStream_t stream);
+hipError_t launch_fwd_bf16_asm(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdArgs& a, int d, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, int d, hipStream_t stream);
 hipError_t launch_bwd_bf16(const BwdArgs& a, int d, hipStream_t stream);

@@ -1,0 +1,596 @@
+"""Generate the gfx950 assembly of one query tile of the d = 128 bf16
+FlashAttention forward (64 query rows per wavefront, one wavefront per SIMD).
+
+    python exact_io_aware_02_amd/gen_fwd_asm.py OUT.inc
+
+The build runs this before compiling fa_fwd_bf16_asm.hip, which includes the
+output: the C string macro FA_ASM_ITEM, the body of one inline-asm statement
+that runs Algorithm 1 of "Infra: Flash Attention" ("Tiled computation and
+forward") without a causal mask for one query tile of a wavefront and leaves
+O = U / l, as bf16 rows, in LDS (keys past N are masked).
+
+Why assembly: a wavefront keeps U^T for 64 queries (128 AGPRs), its Q
+fragments (64 AGPRs), two score tiles and two probability tiles (192 VGPRs)
+live at once.  The compiler spills and copies such a kernel between the
+register files; written out, every value has one home:
+
+  a[0:127]    U^T accumulators, u[db][qb] = a[(2 db + qb) * 16 ...]
+  a[128:191]  Q fragments, qf[qb][ds] = a[128 + (8 qb + ds) * 4 ...]
+  a[192:255]  16 slots of K / V fragments read from LDS
+  v[0:127]    score tiles S_A, S_B: s[cb][qb] = 16 VGPRs at (2 cb + qb) * 16
+  v[128:191]  probability tiles W_A, W_B: w[qb][ks] = 4 VGPRs at (4 qb + ks) * 4
+  v[192:207]  softmax temporaries
+  v[208:223]  per-row state (base m, partial l, alpha, ...)
+
+Each tile step j (64 keys) is one straight-line stream that overlaps, inside
+the wavefront, U += V_{j-1}^T W_{j-1}^T and S_{j+1} = K_{j+1} Q^T on the
+matrix core with the softmax of S_j on the VALU (the FlashAttention-3
+overlap of the blog's FA-3 section as a software pipeline over tiles).  A
+wavefront issues independent VALU instructions while its MFMAs run, so the
+softmax hides under the products.
+
+Hazards the compiler would otherwise handle are handled here:
+  * LDS reads -> MFMA operands: s_waitcnt lgkmcnt counted per read.
+  * MFMA results -> VALU reads: score tiles are read one step (a barrier and
+    more than 50 instructions) after the MFMAs that wrote them; U is read only
+    after 48 wait states.
+  * VALU compare -> lane-mask read, VALU -> permlane: 2 wait states.
+  * transcendental result -> VALU read: at least 1 wait state.
+  * M0 write -> buffer load to LDS: 1 wait state (more are given).
+"""
+
+import sys
+
+D = 128
+BC = 64
+STRIDE = 2 * D + 16          # padded LDS row (bytes)
+TILE = BC * STRIDE           # one K or V tile in LDS (17408)
+KBUF = [0, TILE]             # K buffer offsets from the K read base
+VBUF = [0, TILE]             # V buffer offsets from the V read base
+KV_LDS = [0, TILE, 2 * TILE, 3 * TILE]  # K0, K1, V0, V1 from the LDS base
+LOADS = TILE // 1024         # 17 x 1 KiB buffer->LDS loads per tile
+WAVES = 4
+
+S_BUF = [0, 64]              # VGPR base of S_A, S_B
+W_BUF = [128, 160]           # VGPR base of W_A, W_B
+TMP0 = 192                   # 16 temporaries v[192:207]
+ST = 208                     # state registers v[208:223]
+V_M = [ST + 0, ST + 1]       # base m per query block (raw score units)
+V_L = [ST + 2, ST + 3]       # partial l per query block (this lane's keys)
+V_MC = [ST + 4, ST + 5]      # m * c (VGPR banks 0, 1)
+V_AL = [ST + 6, ST + 7]      # alpha
+V_MX = [ST + 8, ST + 9]      # tile max
+V_NINF = ST + 10             # -inf
+V_THR = [ST + 11, ST + 12]   # mask thresholds
+V_T = ST + 13                # scratch
+V_MC2 = [ST + 14, ST + 15]   # m * c again, in VGPR banks 2, 3
+FRAG0 = 192                  # AGPR fragment slots a[192:255]
+NSLOT = 16
+LOOKAHEAD = 6
+
+# SGPRs used inside (declared as clobbers)
+S_J = 40        # tile index j
+S_T1 = 41
+S_T2 = 42
+S_SOFF = 43     # DMA source offset of a tile
+S_MV = [44, 46]  # moved masks per query block (pairs)
+S_ANY = 48      # pair
+S_CMP = [50, 52, 54]  # compare masks (pairs)
+S_KB = 56       # key base of the masked tile
+S_Q1 = 57       # 8192: byte offset of query block 1
+S_M0 = 58       # the caller's M0, restored at the end
+S_SOFFV = 59    # DMA source offset of a V tile
+S_C = 70        # c = scale * log2(e)
+S_THETA = 71    # rescale threshold (raw score units)
+S_256 = 72      # 2^8 as fp32
+SGPR_CLOBBERS = list(range(40, 60)) + [S_C, S_THETA, S_256]
+
+
+def kfrag_reads(slot, buf, cb, ds):
+    f = FRAG0 + 4 * slot
+    off = KBUF[buf] + cb * 32 * STRIDE + ds * 32
+    return [f"ds_read_b128 a[{f}:{f + 3}], %[kb] offset:{off}"]
+
+
+def vfrag_reads(slot, buf, db, ks):
+    f = FRAG0 + 4 * slot
+    out = []
+    for t in range(2):
+        off = VBUF[buf] + (ks * 16 + 2 * t) * STRIDE + db * 64
+        out.append(f"ds_read_b64_tr_b16 a[{f + 2 * t}:{f + 2 * t + 1}], %[vb] offset:{off}")
+    return out
+
+
+def mfma_pv(slot, db, qb, wbuf, ks):
+    f = FRAG0 + 4 * slot
+    u = (2 * db + qb) * 16
+    w = W_BUF[wbuf] + (4 * qb + ks) * 4
+    return f"v_mfma_f32_32x32x16_bf16 a[{u}:{u + 15}], a[{f}:{f + 3}], v[{w}:{w + 3}], a[{u}:{u + 15}]"
+
+
+def mfma_qk(slot, sbuf, cb, qb, ds):
+    f = FRAG0 + 4 * slot
+    s = S_BUF[sbuf] + (2 * cb + qb) * 16
+    q = 128 + (8 * qb + ds) * 4
+    c = "0" if ds == 0 else f"v[{s}:{s + 15}]"
+    return f"v_mfma_f32_32x32x16_bf16 v[{s}:{s + 15}], a[{f}:{f + 3}], a[{q}:{q + 3}], {c}"
+
+
+def interleave_lists(lists):
+    """Round-robin merge of instruction lists (each list keeps its order)."""
+    out = []
+    for k in range(max(len(x) for x in lists)):
+        for x in lists:
+            if k < len(x):
+                out.append(x[k])
+    return out
+
+
+def softmax_ops(sbuf, wbuf, fast=False):
+    """VALU instructions of the softmax of score tile sbuf into W tile wbuf:
+    row max, the conditional move of the base (threshold theta in raw score
+    units), W = exp2(c S - c m) in bf16, the fp32 row sums, l = alpha l + sum.
+
+    A VALU instruction whose VGPR operands share a bank (register number mod
+    4) pays for the conflict, and one wavefront has no other wavefront to
+    hide that behind, so operands are placed in distinct banks: c is an SGPR,
+    m c has a copy in banks 0/1 and one in 2/3, score pairs use temporaries
+    in banks 0/1 and the partial sums live in banks 2/3, and the max chains
+    combine scores of banks 0 and 2 (resp. 1 and 3) into an accumulator of
+    another bank.  Dependent chains are short and interleaved (eight max
+    chains, eight partial sums).
+
+    fast: W relative to the current base without forming the row max; l is
+    left alone and the tile's per-lane sums are left in psum[0] and psum[4].
+    If no sum exceeds 2^8, no weight did either, and the result is what the
+    full version gives when the base does not move (alpha = 1)."""
+    sb = S_BUF[sbuf]
+    ops = []
+    pair_tmp = [(TMP0 + 4 * i, TMP0 + 4 * i + 1) for i in range(4)]          # banks 0, 1
+    psum = [TMP0 + 4 * (i // 2) + 2 + (i & 1) for i in range(8)]             # banks 2, 3
+    if fast:
+        return exp_ops(sb, wbuf, pair_tmp, psum)
+    # row max: per (query block, 32-key block) two chains, over the scores in
+    # banks {0, 2} (accumulator in bank 1 or 3) and in banks {1, 3}
+    # (accumulator in bank 0 or 2)
+    acc_even = [TMP0 + 1, TMP0 + 3, TMP0 + 5, TMP0 + 7]   # banks 1, 3
+    acc_odd = [TMP0 + 0, TMP0 + 2, TMP0 + 4, TMP0 + 6]    # banks 0, 2
+    chains = []
+    for qb in range(2):
+        for cb in range(2):
+            r = sb + (2 * cb + qb) * 16
+            i = 2 * qb + cb
+            for par, acc in ((0, acc_even[i]), (1, acc_odd[i])):
+                vals = [r + t for t in range(par, 16, 2)]
+                ch = [f"v_max_f32 v{acc}, v{vals[0]}, v{vals[1]}"]
+                for k in range(2, 8, 2):
+                    ch.append(f"v_max3_f32 v{acc}, v{acc}, v{vals[k]}, v{vals[k + 1]}")
+                chains.append(ch)
+    ops += interleave_lists(chains)
+    for qb in range(2):
+        e0, e1 = acc_even[2 * qb], acc_even[2 * qb + 1]
+        o0, o1 = acc_odd[2 * qb], acc_odd[2 * qb + 1]
+        ops.append(f"v_max3_f32 v{o0}, v{o0}, v{e0}, v{e1}")
+        ops.append(f"v_max_f32 v{V_MX[qb]}, v{o0}, v{o1}")
+    for qb in range(2):
+        ops.append(f"v_mov_b32 v{acc_even[qb]}, v{V_MX[qb]}")
+    ops.append("s_nop 1")
+    for qb in range(2):
+        ops.append(f"v_permlane32_swap_b32 v{V_MX[qb]}, v{acc_even[qb]}")
+    for qb in range(2):
+        ops.append(f"v_max_f32 v{V_MX[qb]}, v{V_MX[qb]}, v{acc_even[qb]}")
+    thr = []
+    for qb in range(2):
+        mx, m, mc, mc2, al = V_MX[qb], V_M[qb], V_MC[qb], V_MC2[qb], V_AL[qb]
+        mv = S_MV[qb]
+        t = acc_odd[2 + qb]
+        thr.append([
+            f"v_add_f32 v{t}, s{S_THETA}, v{m}",                    # m + theta
+            f"v_cmp_gt_f32_e64 s[{mv}:{mv + 1}], v{mx}, v{t}",       # moved
+            "s_nop 1",
+            f"v_cndmask_b32_e64 v{mx}, v{m}, v{mx}, s[{mv}:{mv + 1}]",  # m_new
+            f"v_mul_f32 v{mc}, s{S_C}, v{mx}",                      # c m_new
+            f"v_fma_f32 v{t}, v{m}, s{S_C}, -v{mc}",                # c (m_old - m_new)
+            f"v_exp_f32 v{t}, v{t}",
+            f"v_mov_b32 v{mc2}, v{mc}",
+            f"v_mov_b32 v{m}, v{mx}",
+            f"v_cndmask_b32_e64 v{al}, 1.0, v{t}, s[{mv}:{mv + 1}]",  # alpha
+        ])
+    ops += interleave_lists(thr)
+    ops += exp_ops(sb, wbuf, pair_tmp, psum)
+    for qb in range(2):
+        ops.append(f"v_fma_f32 v{V_L[qb]}, v{V_AL[qb]}, v{V_L[qb]}, v{psum[4 * qb]}")
+    return ops
+
+
+def exp_ops(sb, wbuf, pair_tmp, psum):
+    """W = exp2(c S - c m) for a score tile: per pair of scores two FMAs, two
+    exponentials (each read at least one instruction later), two adds into
+    the partial sum of the pair's 8-key group, one bf16 pack; the two query
+    blocks alternate.  Leaves the per-lane tile sums in psum[0], psum[4]."""
+    ops = []
+    seqs = {0: [], 1: []}
+    k_pair = 0
+    for ks in range(4):
+        cb, h = ks >> 1, ks & 1
+        for k in range(4):
+            for qb in range(2):
+                src = sb + (2 * cb + qb) * 16 + 8 * h + 2 * k   # banks 0, 1 (k even) or 2, 3
+                mcx = V_MC2[qb] if k % 2 == 0 else V_MC[qb]
+                w = W_BUF[wbuf] + (4 * qb + ks) * 4
+                a, b = pair_tmp[k_pair % 4]
+                k_pair += 1
+                ps = psum[4 * qb + ks]
+                seqs[qb] += [
+                    f"v_fma_f32 v{a}, v{src}, s{S_C}, -v{mcx}",
+                    f"v_fma_f32 v{b}, v{src + 1}, s{S_C}, -v{mcx}",
+                    f"v_exp_f32 v{a}, v{a}",
+                    f"v_exp_f32 v{b}, v{b}",
+                    f"v_add_f32 v{ps}, 0, v{a}" if k == 0 else f"v_add_f32 v{ps}, v{ps}, v{a}",
+                    f"v_add_f32 v{ps}, v{ps}, v{b}",
+                    f"v_cvt_pk_bf16_f32 v{w + k}, v{a}, v{b}",
+                ]
+    for i in range(0, len(seqs[0]), 7):
+        ops += seqs[0][i:i + 7] + seqs[1][i:i + 7]
+    for qb in range(2):
+        p = psum[4 * qb:4 * qb + 4]
+        ops += [f"v_add_f32 v{p[0]}, v{p[0]}, v{p[1]}", f"v_add_f32 v{p[2]}, v{p[2]}, v{p[3]}"]
+    for qb in range(2):
+        p = psum[4 * qb:4 * qb + 4]
+        ops.append(f"v_add_f32 v{p[0]}, v{p[0]}, v{p[2]}")
+    return ops
+
+
+class Stream:
+    """Builds one straight-line block: MFMAs with their fragment reads issued
+    LOOKAHEAD fragments ahead, lgkmcnt waits counted per read, and VALU
+    instructions spread evenly between the MFMAs."""
+
+    def __init__(self):
+        self.out = []
+
+    def emit(self, s):
+        self.out.append(s)
+
+    def block(self, frags, valu, valu_first=0, groups=()):
+        """frags: list of (read_fn(slot) -> [instr], [mfma_fn(slot) -> instr]);
+        groups: instruction groups (buffer->LDS loads) issued one after each
+        odd MFMA, so the matrix core runs while the wavefront issues them."""
+        issued = []      # per issued DS instruction: fragment index
+        n = len(frags)
+        nmf = sum(len(m) for _, m in frags)
+        next_read = 0
+        vi = 0
+
+        def read_upto(k):
+            nonlocal next_read
+            while next_read < n and next_read <= k:
+                rd, _ = frags[next_read]
+                for ins in rd(next_read % NSLOT):
+                    self.emit(ins)
+                    issued.append(next_read)
+                next_read += 1
+
+        ready = set()
+        gi = 0
+        read_upto(LOOKAHEAD - 1)
+        while vi < min(valu_first, len(valu)):
+            self.emit(valu[vi])
+            vi += 1
+        done = 0
+        for fi, (_, mfs) in enumerate(frags):
+            read_upto(fi + LOOKAHEAD - 1)
+            if fi not in ready:
+                # wait for this fragment and the next one
+                upto = fi + 1 if fi + 1 < next_read else fi
+                last = max(i for i, f in enumerate(issued) if f == upto)
+                after = len(issued) - 1 - last
+                self.emit(f"s_waitcnt lgkmcnt({min(after, 15)})")
+                ready.update(range(fi, upto + 1))
+            for mf in mfs:
+                self.emit(mf(fi % NSLOT))
+                done += 1
+                while gi < len(groups) and done >= (gi + 1) * nmf // (len(groups) + 1):
+                    for ins in groups[gi]:
+                        self.emit(ins)
+                    gi += 1
+                target = valu_first + ((len(valu) - valu_first) * done + nmf - 1) // nmf
+                while vi < min(target, len(valu)):
+                    self.emit(valu[vi])
+                    vi += 1
+        while vi < len(valu):
+            self.emit(valu[vi])
+            vi += 1
+        assert gi == len(groups), "load groups left over"
+
+
+def pv_frags(vbuf, wbuf):
+    fr = []
+    for ks in range(4):
+        for db in range(4):
+            fr.append((lambda s, ks=ks, db=db: vfrag_reads(s, vbuf, db, ks),
+                       [lambda s, db=db, qb=qb, ks=ks: mfma_pv(s, db, qb, wbuf, ks) for qb in range(2)]))
+    return fr
+
+
+def qk_frags(kbuf, sbuf):
+    fr = []
+    for ds in range(8):
+        for cb in range(2):
+            fr.append((lambda s, cb=cb, ds=ds: kfrag_reads(s, kbuf, cb, ds),
+                       [lambda s, cb=cb, qb=qb, ds=ds: mfma_qk(s, sbuf, cb, qb, ds) for qb in range(2)]))
+    return fr
+
+
+def interleave(a, b):
+    out = []
+    for x, y in zip(a, b):
+        out += [x, y]
+    return out
+
+
+def dma_groups(kind, dst_off, soff_sgpr):
+    """Buffer->LDS loads of one K or V tile as instruction groups: this
+    wavefront's 1 KiB blocks wave, wave + 4, ...; block 16 belongs to
+    wavefront 0, so the other wavefronts issue that load with no lane active
+    (EXEC = 0: nothing is read or written).  The source offset of the tile is
+    in s[soff_sgpr]."""
+    rs = "%[krsrc]" if kind == "k" else "%[vrsrc]"
+    out = []
+    for p in range((LOADS + WAVES - 1) // WAVES):
+        g = []
+        partial = WAVES * p + WAVES > LOADS
+        if partial:
+            g += ["s_cmp_eq_u32 %[wave], 0", "s_cselect_b64 exec, -1, 0", "s_nop 4"]
+        g += [f"s_add_u32 m0, %[wbase], {dst_off + p * WAVES * 1024}", "s_nop 1",
+              f"buffer_load_dwordx4 %[{kind}vo{p}], {rs}, s{soff_sgpr} offen lds"]
+        if partial:
+            g += ["s_mov_b64 exec, -1", "s_nop 4"]
+        out.append(g)
+    return out
+
+
+def dma_tile(st, kind, dst_off, tile_sgpr_expr, label):
+    """Buffer->LDS loads of one K or V tile: this wavefront's 1 KiB blocks
+    wave, wave + 4, ... (block 16 only on wavefront 0)."""
+    st.emit(f"s_lshl_b32 s{S_SOFF}, {tile_sgpr_expr}, {14}")
+    for p in range((LOADS + WAVES - 1) // WAVES):
+        if WAVES * p + WAVES > LOADS:
+            st.emit("s_cmp_lg_u32 %[wave], 0")
+            st.emit(f"s_cbranch_scc1 {label}_%=")
+        st.emit(f"s_add_u32 m0, %[wbase], {dst_off + p * WAVES * 1024}")
+        st.emit("s_nop 1")
+        rs = "%[krsrc]" if kind == "k" else "%[vrsrc]"
+        st.emit(f"buffer_load_dwordx4 %[{kind}vo{p}], {rs}, s{S_SOFF} offen lds")
+    st.emit(f"{label}_%=:")
+
+
+def mask_block(st, sbuf, causal, label):
+    """Scores of the tile at key base 64 j (in s[S_J]) set to -inf where the
+    key is past the last valid one of the lane's query: key kbase + c + 4 g
+    against lim (thresholds in %[limg0/1] = lim - 4 g)."""
+    st.emit(f"s_lshl_b32 s{S_KB}, s{S_J}, 6")
+    # skip unless the tile reaches past a row's limit: causal kbase + 63 > qw0,
+    # or kbase + 64 > N
+    st.emit(f"s_add_u32 s{S_T1}, s{S_KB}, 64")
+    st.emit(f"s_cmp_gt_u32 s{S_T1}, %[n_keys]")
+    st.emit(f"s_cbranch_scc1 {label}_do_%=")
+    if causal:
+        st.emit(f"s_add_u32 s{S_T1}, s{S_KB}, 63")
+        st.emit(f"s_cmp_gt_u32 s{S_T1}, %[qw0]")
+        st.emit(f"s_cbranch_scc1 {label}_do_%=")
+    st.emit(f"s_branch {label}_end_%=")
+    st.emit(f"{label}_do_%=:")
+    st.emit("s_nop 15")
+    st.emit("s_nop 15")
+    st.emit("s_nop 15")
+    for qb in range(2):
+        st.emit(f"v_subrev_u32 v{V_THR[qb]}, s{S_KB}, %[limg{qb}]")
+    k = 0
+    pend = []
+    sb = S_BUF[sbuf]
+    for qb in range(2):
+        for cb in range(2):
+            for i in range(16):
+                c = 32 * cb + 8 * (i >> 2) + (i & 3)
+                reg = sb + (2 * cb + qb) * 16 + i
+                sp = S_CMP[k % 3]
+                st.emit(f"v_cmp_lt_i32_e64 s[{sp}:{sp + 1}], v{V_THR[qb]}, {c}")
+                pend.append((reg, sp))
+                k += 1
+                if len(pend) == 3:
+                    for r, s in pend:
+                        st.emit(f"v_cndmask_b32_e64 v{r}, v{r}, v{V_NINF}, s[{s}:{s + 1}]")
+                    pend = []
+    for r, s in pend:
+        st.emit("s_nop 1")
+        st.emit(f"v_cndmask_b32_e64 v{r}, v{r}, v{V_NINF}, s[{s}:{s + 1}]")
+    st.emit(f"{label}_end_%=:")
+
+
+def rescale_block(st, label):
+    st.emit(f"s_or_b64 s[{S_ANY}:{S_ANY + 1}], s[{S_MV[0]}:{S_MV[0] + 1}], s[{S_MV[1]}:{S_MV[1] + 1}]")
+    st.emit(f"s_cbranch_scc0 {label}_%=")
+    st.emit("s_nop 15")
+    st.emit("s_nop 15")
+    st.emit("s_nop 15")
+    for base in range(0, 128, 8):
+        qb = (base // 16) % 2
+        for k in range(8):
+            st.emit(f"v_accvgpr_read_b32 v{TMP0 + k}, a{base + k}")
+        for k in range(8):
+            st.emit(f"v_mul_f32 v{TMP0 + k}, v{TMP0 + k}, v{V_AL[qb]}")
+        for k in range(8):
+            st.emit(f"v_accvgpr_write_b32 a{base + k}, v{TMP0 + k}")
+    st.emit("s_nop 3")
+    st.emit(f"{label}_%=:")
+
+
+def step(st, parity, causal, kind, label):
+    """Tile step j (parity = j & 1, j in s[S_J]).  kind: 'full' (PV of j-1,
+    QK of j+1, softmax of j), 'last' (PV of j-1, softmax of j), 'first'
+    (j = 0: QK of 1, softmax of 0)."""
+    j_odd = parity
+    # top: own loads landed, every wavefront done with step j-1's buffers
+    st.emit("s_waitcnt vmcnt(0) lgkmcnt(0)")
+    st.emit("s_barrier")
+    groups = []
+    if kind in ("full", "first"):
+        # K_{j+2} into K buffer j & 1, last read in step j-1.  Past the last
+        # tile it reads zeros (or unneeded keys) into a buffer nobody reads.
+        st.emit(f"s_add_u32 s{S_T2}, s{S_J}, 2")
+        st.emit(f"s_lshl_b32 s{S_SOFF}, s{S_T2}, 14")
+        groups += dma_groups("k", KV_LDS[j_odd], S_SOFF)
+    if kind in ("full", "last"):
+        # V_j into V buffer j & 1, last read (V_{j-2}) in step j-1
+        st.emit(f"s_lshl_b32 s{S_SOFFV}, s{S_J}, 14")
+        groups += dma_groups("v", KV_LDS[2 + j_odd], S_SOFFV)
+    mask_block(st, j_odd, causal, f"{label}_mask")
+    valu = softmax_ops(j_odd, j_odd, fast=(kind != "first"))
+    if kind == "full":
+        frags = interleave(pv_frags(1 - j_odd, 1 - j_odd), qk_frags(1 - j_odd, 1 - j_odd))
+    elif kind == "last":
+        frags = pv_frags(1 - j_odd, 1 - j_odd)
+    else:
+        frags = qk_frags(1, 1)
+    st.block(frags, valu, valu_first=(40 if kind == "first" else 8), groups=groups)
+    if kind != "first":
+        # conditional rescaling ("Invariant of conditional rescaling"): the
+        # base moves only if a weight relative to it exceeds 2^8, which only
+        # a tile sum above 2^8 can show; then the tile's softmax is redone
+        # with its row max, and U and l are rescaled
+        t0, t1 = TMP0 + 2, TMP0 + 10   # psum[0], psum[4]
+        st.emit(f"v_cmp_gt_f32_e64 s[{S_MV[0]}:{S_MV[0] + 1}], v{t0}, s{S_256}")
+        st.emit(f"v_cmp_gt_f32_e64 s[{S_MV[1]}:{S_MV[1] + 1}], v{t1}, s{S_256}")
+        st.emit("s_nop 1")
+        st.emit(f"s_or_b64 s[{S_ANY}:{S_ANY + 1}], s[{S_MV[0]}:{S_MV[0] + 1}], s[{S_MV[1]}:{S_MV[1] + 1}]")
+        st.emit(f"s_cbranch_scc1 {label}_slow_%=")
+        st.emit(f"v_add_f32 v{V_L[0]}, v{V_L[0]}, v{t0}")
+        st.emit(f"v_add_f32 v{V_L[1]}, v{V_L[1]}, v{t1}")
+        st.emit(f"s_branch {label}_done_%=")
+        st.emit(f"{label}_slow_%=:")
+        for ins in softmax_ops(j_odd, j_odd):
+            st.emit(ins)
+        rescale_block(st, f"{label}_rs")
+        st.emit(f"{label}_done_%=:")
+
+
+def item_asm(causal):
+    st = Stream()
+    e = st.emit
+    e(f"s_mov_b32 s{S_M0}, m0")
+    e(f"v_readfirstlane_b32 s{S_C}, %[c]")
+    e(f"v_readfirstlane_b32 s{S_THETA}, %[theta]")
+    e(f"s_mov_b32 s{S_256}, 0x43800000")
+    e(f"v_mov_b32 v{V_NINF}, 0xff800000")
+    e(f"v_mov_b32 v{V_M[0]}, 0xff800000")
+    e(f"v_mov_b32 v{V_M[1]}, 0xff800000")
+    e(f"v_mov_b32 v{V_L[0]}, 0")
+    e(f"v_mov_b32 v{V_L[1]}, 0")
+    for k in range(128):
+        e(f"v_accvgpr_write_b32 a{k}, 0")
+    # Q fragments into AGPRs (rows past N read as zeros)
+    e(f"s_movk_i32 s{S_Q1}, 0x2000")
+    for qb in range(2):
+        for ds in range(8):
+            q = 128 + (8 * qb + ds) * 4
+            so = "0" if qb == 0 else f"s{S_Q1}"
+            e(f"buffer_load_dwordx4 a[{q}:{q + 3}], %[qvo], %[qrsrc], {so} offen offset:{32 * ds}")
+    # K_0, V_0, K_1
+    e(f"s_mov_b32 s{S_J}, 0")
+    dma_tile(st, "k", KV_LDS[0], f"s{S_J}", "pk0")
+    dma_tile(st, "v", KV_LDS[2], f"s{S_J}", "pv0")
+    e(f"s_mov_b32 s{S_T2}, 1")
+    dma_tile(st, "k", KV_LDS[1], f"s{S_T2}", "pk1")
+    e("s_waitcnt vmcnt(0)")
+    e("s_barrier")
+    # S_0 = K_0 Q^T
+    st.block(qk_frags(0, 0), [])
+    e("s_nop 15")
+    e("s_nop 15")
+    # step 0
+    step(st, 0, causal, "first", "st0")
+    e("s_cmp_eq_u32 %[n], 1")
+    e("s_cbranch_scc1 L_fin0_%=")
+    e(f"s_mov_b32 s{S_J}, 1")
+    e("L_loop_%=:")
+    e(f"s_add_u32 s{S_T1}, s{S_J}, 1")
+    e(f"s_cmp_lt_u32 s{S_T1}, %[n]")
+    e("s_cbranch_scc0 L_last1_%=")
+    step(st, 1, causal, "full", "sa")
+    e(f"s_add_u32 s{S_J}, s{S_J}, 1")
+    e(f"s_add_u32 s{S_T1}, s{S_J}, 1")
+    e(f"s_cmp_lt_u32 s{S_T1}, %[n]")
+    e("s_cbranch_scc0 L_last0_%=")
+    step(st, 0, causal, "full", "sb")
+    e(f"s_add_u32 s{S_J}, s{S_J}, 1")
+    e("s_branch L_loop_%=")
+    # last step j = n - 1 (odd), then U += V_{n-1} W_{n-1} from buffers 1
+    e("L_last1_%=:")
+    step(st, 1, causal, "last", "sl1")
+    e("s_waitcnt vmcnt(0) lgkmcnt(0)")
+    e("s_barrier")
+    st.block(pv_frags(1, 1), [])
+    e("s_branch L_done_%=")
+    e("L_last0_%=:")
+    step(st, 0, causal, "last", "sl0")
+    e("L_fin0_%=:")
+    e("s_waitcnt vmcnt(0) lgkmcnt(0)")
+    e("s_barrier")
+    st.block(pv_frags(0, 0), [])
+    e("L_done_%=:")
+    # epilogue: every wavefront done with the K/V area; O = U / l into this
+    # wavefront's 64 staging rows (l summed over the lane pair first)
+    e("s_waitcnt lgkmcnt(0)")
+    e("s_barrier")
+    for qb in range(2):
+        e(f"v_mov_b32 v{V_T}, v{V_L[qb]}")
+        e("s_nop 1")
+        e(f"v_permlane32_swap_b32 v{V_L[qb]}, v{V_T}")
+        e(f"v_add_f32 v{V_L[qb]}, v{V_L[qb]}, v{V_T}")
+        e(f"v_rcp_f32 v{V_AL[qb]}, v{V_L[qb]}")
+    e("s_nop 15")
+    e("s_nop 15")
+    e("s_nop 15")
+    for qb in range(2):
+        for db in range(4):
+            u = (2 * db + qb) * 16
+            for i4 in range(4):
+                for k in range(4):
+                    e(f"v_accvgpr_read_b32 v{TMP0 + k}, a{u + 4 * i4 + k}")
+                for k in range(4):
+                    e(f"v_mul_f32 v{TMP0 + k}, v{TMP0 + k}, v{V_AL[qb]}")
+                e(f"v_cvt_pk_bf16_f32 v{TMP0 + 4}, v{TMP0}, v{TMP0 + 1}")
+                e(f"v_cvt_pk_bf16_f32 v{TMP0 + 5}, v{TMP0 + 2}, v{TMP0 + 3}")
+                off = qb * 32 * STRIDE + 64 * db + 16 * i4
+                e(f"ds_write_b64 %[stg], v[{TMP0 + 4}:{TMP0 + 5}] offset:{off}")
+    e("s_waitcnt lgkmcnt(0)")
+    e(f"v_mov_b32 %[mo0], v{V_M[0]}")
+    e(f"v_mov_b32 %[mo1], v{V_M[1]}")
+    e(f"v_mov_b32 %[lo0], v{V_L[0]}")
+    e(f"v_mov_b32 %[lo1], v{V_L[1]}")
+    e(f"s_mov_b32 m0, s{S_M0}")
+    return st.out
+
+
+def clobbers():
+    v = [f'"v{i}"' for i in range(0, ST + 16)]
+    a = [f'"a{i}"' for i in range(256)]
+    s = [f'"s{i}"' for i in SGPR_CLOBBERS]
+    return ", ".join(v + a + s + ['"vcc"', '"scc"', '"memory"'])
+
+
+def main(out):
+    with open(out, "w") as f:
+        f.write("// Generated by gen_fwd_asm.py; do not edit.\n#pragma once\n\n")
+        for name, causal in (("FA_ASM_ITEM", False),):
+            body = item_asm(causal)
+            f.write(f"#define {name} \\\n")
+            for ins in body:
+                f.write(f'  "{ins}\\n" \\\n')
+            f.write('  ""\n\n')
+        f.write(f"#define FA_ASM_CLOBBERS {clobbers()}\n")
+
+
+if __name__ == "__main__":
+    main(sys.argv[1])

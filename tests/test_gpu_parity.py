@@ -183,7 +183,7 @@ def test_bf16_causal_many_items_per_workgroup(B, H, N):
 
 
 def test_bf16_large_values_and_scale():
-    """Scores with a wide spread (values x4, scale 0.5) exercise the running
+    """Scores with a wide spread (values x4, scale 0.05) exercise the running
     maximum and the alpha rescale across many tiles."""
     fa = _fa()
     _say("bf16 wide scores")
@@ -196,6 +196,33 @@ def test_bf16_large_values_and_scale():
         torch.cuda.synchronize()
         dO, dL = _prefill_compare(Q, K, V, O, L, 0.05, causal)
         assert dO <= 4 * BF16_O and dL <= BF16_L, (causal, dO, dL)
+
+
+@pytest.mark.parametrize("N", [1000, 2049])
+def test_bf16_base_moves_in_later_tiles(N):
+    """Keys grow along the sequence (key j scaled by 1 + 7 j / N), so later
+    KV tiles hold scores far above the first tile's maximum: the running base
+    moves mid-row, after U and l have been accumulated, and U and l must be
+    rescaled ("Invariant of conditional rescaling").  Such peaked rows make O
+    nearly one row of V, so V is halved (exactly) to keep |O| under 4, where
+    the bf16 output rounding leaves room in the 2e-2 bar: at |O| >= 4 half an
+    ulp of bf16 is already 0.0156, and both forward kernels then measure
+    0.0219 on this input."""
+    fa = _fa()
+    _say("bf16 base moves in later tiles", N)
+    shape = (1, 4, N, 128)
+    Q, K, V = (synth.torch_normal(800 + t, shape, "cuda", "f32") for t in range(3))
+    ramp = 1.0 + 7.0 * torch.arange(N, device="cuda", dtype=torch.float32) / N
+    K = K * ramp[None, None, :, None]
+    V = V * 0.5
+    Q, K, V = (t.to(torch.bfloat16) for t in (Q, K, V))
+    O = torch.empty_like(Q)
+    L = torch.empty(shape[:3], device="cuda")
+    for causal in (False, True):
+        fa.fa_fwd(Q, K, V, O, L, causal=causal)
+        torch.cuda.synchronize()
+        dO, dL = _prefill_compare(Q, K, V, O, L, 1 / math.sqrt(128), causal)
+        assert dO <= BF16_O and dL <= BF16_L, (causal, dO, dL)
 
 
 def test_bf16_L_optional_and_deterministic():
