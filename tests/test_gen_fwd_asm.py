@@ -1,0 +1,254 @@
+"""Checks, on the CPU, the generated assembly of the 64-rows-per-wavefront
+forward's tile loop (exact_io_aware_02_amd/gen_fwd_asm.py) against the
+rules the generator states for the hazards it handles itself:
+
+  * every LDS read has landed (s_waitcnt lgkmcnt) before an MFMA or VALU
+    instruction reads the registers it writes;
+  * an MFMA result is not read or overwritten by a non-MFMA instruction
+    within 18 wait states, and the U accumulators are read only after the
+    48 wait states of three s_nop 15;
+  * a transcendental (v_exp_f32, v_rcp_f32) result is not read by the next
+    instruction;
+  * a lane mask written by a VALU compare is read 2 wait states later at the
+    earliest, and so are the operands of v_permlane32_swap;
+  * a VALU write reaches an MFMA operand 2 wait states later at the earliest;
+  * M0 and EXEC writes precede the buffer load that uses them by at least 1
+    and 5 wait states;
+  * the register homes do not overlap, and nothing but the output operands
+    is written outside the clobbered registers.
+
+Wait states are counted along the straight-line order of the program (an
+s_nop N counts N + 1, every other instruction at least 1).  Across the loop's
+back edge a score tile is read a step (a workgroup barrier) after it was
+written, which this linear count does not see and does not need to.
+"""
+
+import importlib.util
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+GEN_PATH = os.path.join(ROOT, "exact_io_aware_02_amd", "gen_fwd_asm.py")
+
+
+def _gen():
+    spec = importlib.util.spec_from_file_location("_gen_fwd_asm", GEN_PATH)
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+REG = re.compile(r"\b([vas])(?:\[(\d+):(\d+)\]|(\d+)\b)")
+
+
+def _regs(text):
+    out = set()
+    for kind, lo, hi, one in REG.findall(text):
+        if one:
+            out.add((kind, int(one)))
+        else:
+            out.update((kind, r) for r in range(int(lo), int(hi) + 1))
+    return out
+
+
+def _parse(line):
+    """(mnemonic, written registers, read registers) of one instruction."""
+    if line.endswith(":"):
+        return ("label", set(), set())
+    op, _, rest = line.partition(" ")
+    args = [a.strip() for a in rest.split(",")] if rest else []
+    no_dst = op.startswith(("s_cmp", "s_cbranch", "s_branch", "s_waitcnt", "s_nop", "s_barrier",
+                            "ds_write", "s_setprio"))
+    if op.startswith("buffer_load") and rest.endswith("lds"):
+        no_dst = True
+    if no_dst or not args:
+        return (op, set(), _regs(rest))
+    dst = _regs(args[0])
+    src = set().union(*[_regs(a) for a in args[1:]]) if len(args) > 1 else set()
+    if op == "v_permlane32_swap_b32":  # swaps: both operands are read and written
+        dst |= src
+        src |= dst
+    return (op, dst, src)
+
+
+def _wait_states(op, line):
+    if op == "s_nop":
+        return int(line.split()[1]) + 1
+    return 1
+
+
+@pytest.fixture(scope="module")
+def program():
+    g = _gen()
+    return g, [ln for ln in g.item_asm(False)]
+
+
+def test_register_homes_are_disjoint(program):
+    g, _ = program
+    vhomes = {
+        "S": set(range(g.S_BUF[0], g.S_BUF[1] + 64)),
+        "W": set(range(g.W_BUF[0], g.W_BUF[1] + 32)),
+        "tmp": set(range(g.TMP0, g.TMP0 + 16)),
+        "state": set(range(g.ST, g.ST + 16)),
+    }
+    names = list(vhomes)
+    for i, a in enumerate(names):
+        for b in names[i + 1:]:
+            assert not (vhomes[a] & vhomes[b]), (a, b)
+    assert g.FRAG0 + 4 * g.NSLOT == 256
+
+
+def test_writes_stay_inside_the_clobbers(program):
+    g, prog = program
+    clob = set()
+    for name in re.findall(r'"(\w+)"', g.clobbers()):
+        m = re.fullmatch(r"([vas])(\d+)", name)
+        if m:
+            clob.add((m.group(1), int(m.group(2))))
+    for line in prog:
+        op, dst, _ = _parse(line)
+        if "%[" in line.split(",")[0]:
+            continue  # the output operands (and M0) are the compiler's
+        for r in dst:
+            assert r in clob, (line, r)
+
+
+def lds_violations(prog):
+    """Reads or overwrites of registers an outstanding LDS read writes."""
+    out, pending = [], []  # registers written by outstanding LDS reads, oldest first
+    for line in prog:
+        op, dst, src = _parse(line)
+        if op == "s_waitcnt":
+            m = re.search(r"lgkmcnt\((\d+)\)", line)
+            if m:
+                keep = int(m.group(1))
+                pending = pending[len(pending) - keep:] if keep < len(pending) else pending
+            continue
+        if op == "label":
+            continue
+        busy = set().union(*pending) if pending else set()
+        if (src & busy) or ((dst & busy) and not op.startswith("ds_read")):
+            out.append(line)
+        if op.startswith("ds_read"):
+            pending.append(dst)
+        elif op.startswith("ds_write"):
+            pending.append(set())
+    return out
+
+
+def mfma_violations(prog):
+    """Non-MFMA reads or writes of an MFMA result within 18 wait states (48
+    for the U accumulators read by v_accvgpr_read)."""
+    out, recent = [], []  # (registers, wait states since the MFMA issued)
+    for line in prog:
+        op, dst, src = _parse(line)
+        if op == "label":
+            continue
+        if op.startswith("v_mfma"):
+            # an MFMA may read (SrcC) and rewrite an accumulator it chains on
+            recent = [(r, w) for r, w in recent if not (r & dst)]
+        else:
+            for regs, w in recent:
+                u = any(k == "a" and n < 128 for k, n in regs) and op == "v_accvgpr_read_b32"
+                if w < (48 if u else 18) and (regs & (src | dst)):
+                    out.append(line)
+        ws = _wait_states(op, line)
+        recent = [(r, w + ws) for r, w in recent]
+        if op.startswith("v_mfma"):
+            recent.append((dst, 0))
+    return out
+
+
+def line_writes(line, reg):
+    parts = line.split(None, 1)
+    return len(parts) == 2 and parts[0].startswith("s_") and parts[1].split(",")[0].strip() == reg
+
+
+def short_range_violations(prog):
+    out = []
+    lines = [ln for ln in prog if not ln.endswith(":")]
+    parsed = [_parse(ln) for ln in lines]
+    for i, (op, dst, src) in enumerate(parsed):
+        def gap_to(j):
+            return sum(_wait_states(parsed[k][0], lines[k]) for k in range(i + 1, j))
+        if op in ("v_exp_f32", "v_rcp_f32", "v_log_f32") and i + 1 < len(parsed) and (parsed[i + 1][2] & dst):
+            out.append(lines[i + 1])
+        for j in range(i + 1, min(i + 4, len(parsed))):
+            opj, dstj, srcj = parsed[j]
+            if op.startswith("v_cmp") and (srcj & dst) and gap_to(j) < 2:
+                out.append(lines[j])
+            if opj == "v_permlane32_swap_b32" and op.startswith("v_") and (dst & srcj) and gap_to(j) < 2:
+                out.append(lines[j])
+            if (opj.startswith("v_mfma") and op.startswith("v_") and not op.startswith("v_mfma")
+                    and (dst & srcj) and gap_to(j) < 2):
+                out.append(lines[j])
+        for reg, need in (("m0", 1), ("exec", 5)):
+            if line_writes(lines[i], reg) and (reg == "m0" or "-1, 0" in lines[i]):
+                j = next((k for k in range(i + 1, len(parsed)) if parsed[k][0].startswith("buffer_load")), None)
+                if j is not None and gap_to(j) < need:
+                    out.append(lines[j])
+    return out
+
+
+def test_lds_reads_land_before_use(program):
+    _, prog = program
+    assert lds_violations(prog) == []
+
+
+def test_mfma_results_settle_before_other_use(program):
+    _, prog = program
+    assert mfma_violations(prog) == []
+
+
+def test_short_range_hazards(program):
+    _, prog = program
+    assert short_range_violations(prog) == []
+
+
+def test_checks_catch_planted_mistakes(program):
+    """Each check rejects a copy of the program with one wait taken out or one
+    instruction moved too close (the checks are not vacuous)."""
+    _, prog = program
+    # an LDS wait removed
+    i = next(k for k, ln in enumerate(prog) if ln.startswith("s_waitcnt lgkmcnt(") and prog[k + 1].startswith("v_mfma"))
+    assert lds_violations(prog[:i] + prog[i + 1:])
+    # a score read right after the MFMA that writes it
+    i = next(k for k, ln in enumerate(prog) if ln.startswith("v_mfma_f32_32x32x16_bf16 v[0:15]"))
+    assert mfma_violations(prog[:i + 1] + ["v_max_f32 v200, v0, v1"] + prog[i + 1:])
+    # a U accumulator read 20 wait states after the MFMA that writes it
+    i = next(k for k, ln in enumerate(prog) if ln.startswith("v_mfma_f32_32x32x16_bf16 a[0:15]"))
+    assert mfma_violations(prog[:i + 1] + ["s_nop 15", "s_nop 3", "v_accvgpr_read_b32 v192, a0"] + prog[i + 1:])
+    # the nop between a compare and its mask's reader removed
+    i = next(k for k, ln in enumerate(prog) if ln.startswith("v_cmp_gt_f32_e64") and prog[k + 1] == "s_nop 1"
+             and prog[k + 2].startswith("s_or_b64"))
+    assert short_range_violations(prog[:i + 1] + prog[i + 2:])
+    # an exponential's result read at once
+    i = next(k for k, ln in enumerate(prog) if ln.startswith("v_exp_f32"))
+    dst = prog[i].split()[1].rstrip(",")
+    assert short_range_violations(prog[:i + 1] + [f"v_add_f32 v200, v200, {dst}"] + prog[i + 1:])
+    # the nops after an EXEC change removed
+    i = next(k for k, ln in enumerate(prog) if ln.startswith("s_cselect_b64 exec"))
+    assert short_range_violations(prog[:i + 1] + prog[i + 2:])
+
+
+def test_every_exec_change_is_undone_before_vector_work(program):
+    _, prog = program
+    masked = False
+    for line in prog:
+        op, _, _ = _parse(line)
+        if line_writes(line, "exec"):
+            masked = "-1, 0" in line
+            continue
+        if masked:
+            assert op.startswith(("s_", "buffer_load")), f"vector work with EXEC changed: {line}"
+
+
+def test_generator_output_is_deterministic(tmp_path):
+    g = _gen()
+    a, b = tmp_path / "a.inc", tmp_path / "b.inc"
+    g.main(str(a))
+    g.main(str(b))
+    assert a.read_text() == b.read_text()
+    assert "FA_ASM_ITEM" in a.read_text() and "FA_ASM_CLOBBERS" in a.read_text()
