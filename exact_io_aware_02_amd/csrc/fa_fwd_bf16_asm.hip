@@ -83,8 +83,11 @@ void fwd_bf16_asm_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict
     const int qw0 = __builtin_amdgcn_readfirstlane(qt * kBR + wave * 64);
     const int n = (N + kBC - 1) / kBC;
     const u32x4_t q_rsrc = make_rsrc(Qg + head_off, head_bytes);
-    const u32x4_t k_rsrc = make_rsrc(Kg + head_off, head_bytes);
-    const u32x4_t v_rsrc = make_rsrc(Vg + head_off, head_bytes);
+    // K and V head bases: the loop builds each tile's resource from them
+    const unsigned long long ka = (unsigned long long)(Kg + head_off);
+    const unsigned long long va = (unsigned long long)(Vg + head_off);
+    const unsigned klo = (unsigned)ka, khi = (unsigned)(ka >> 32) & 0xFFFFu;
+    const unsigned vlo = (unsigned)va, vhi = (unsigned)(va >> 32) & 0xFFFFu;
     const unsigned qvo = (unsigned)(qw0 + l32) * D * 2 + g * 16;
     // keys past N are masked: the loop compares key - 4 g against N - 1 - 4 g
     const int limg = N - 1 - 4 * g;
@@ -95,7 +98,8 @@ void fwd_bf16_asm_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict
                    [kvo4] "v"(kvo[4]), [vvo0] "v"(vvo[0]), [vvo1] "v"(vvo[1]), [vvo2] "v"(vvo[2]),
                    [vvo3] "v"(vvo[3]), [vvo4] "v"(vvo[4]), [qvo] "v"(qvo), [kb] "v"(kb), [vb] "v"(vb),
                    [stg] "v"(stg), [limg0] "v"(limg), [limg1] "v"(limg), [qrsrc] "s"(q_rsrc),
-                   [krsrc] "s"(k_rsrc), [vrsrc] "s"(v_rsrc), [n] "s"(n), [c] "v"(c), [theta] "v"(theta),
+                   [klo] "s"(klo), [khi] "s"(khi), [vlo] "s"(vlo), [vhi] "s"(vhi), [hb] "s"(head_bytes),
+                   [n] "s"(n), [c] "v"(c), [theta] "v"(theta),
                    [wave] "s"(wave), [wbase] "s"(wbase), [n_keys] "s"(N), [qw0] "s"(qw0)
                  : FA_ASM_CLOBBERS);
     // the wavefront's 64 rows of O wait in its staging rows (written and

@@ -37,6 +37,14 @@ Hazards the compiler would otherwise handle are handled here:
   * VALU compare -> lane-mask read, VALU -> permlane: 2 wait states.
   * transcendental result -> VALU read: at least 1 wait state.
   * M0 write -> buffer load to LDS: 1 wait state (more are given).
+
+Buffer loads are bounds-checked by the hardware against the size in their
+resource through their VGPR and instruction offsets (whether the SGPR offset
+counts differs between GPU generations).  So each K or V tile is loaded
+through a resource of its own that starts at the tile and ends at the end of
+the head (empty past it), and the second query block's rows are addressed
+through a VGPR: rows past N read as zeros and no load touches memory past
+the head, by construction.
 """
 
 import sys
@@ -72,18 +80,18 @@ LOOKAHEAD = 6
 S_J = 40        # tile index j
 S_T1 = 41
 S_T2 = 42
-S_SOFF = 43     # DMA source offset of a tile
+S_SOFF = 43     # byte offset of a tile within the head
 S_MV = [44, 46]  # moved masks per query block (pairs)
 S_ANY = 48      # pair
 S_CMP = [50, 52, 54]  # compare masks (pairs)
 S_KB = 56       # key base of the masked tile
-S_Q1 = 57       # 8192: byte offset of query block 1
 S_M0 = 58       # the caller's M0, restored at the end
-S_SOFFV = 59    # DMA source offset of a V tile
 S_C = 70        # c = scale * log2(e)
 S_THETA = 71    # rescale threshold (raw score units)
 S_256 = 72      # 2^8 as fp32
-SGPR_CLOBBERS = list(range(40, 60)) + [S_C, S_THETA, S_256]
+S_RK = 60       # s[60:63]: resource of the K tile being loaded
+S_RV = 64       # s[64:67]: resource of the V tile being loaded
+SGPR_CLOBBERS = list(range(40, 59)) + list(range(60, 68)) + [S_C, S_THETA, S_256]
 
 
 def kfrag_reads(slot, buf, cb, ds):
@@ -329,13 +337,24 @@ def interleave(a, b):
     return out
 
 
-def dma_groups(kind, dst_off, soff_sgpr):
+def tile_rsrc(emit, kind, tile_sgpr, r):
+    """s[r:r+3] = resource of K or V tile s[tile_sgpr] of the head: base at
+    the tile, size the bytes left in the head (0 past its end)."""
+    emit(f"s_lshl_b32 s{S_SOFF}, s{tile_sgpr}, 14")
+    emit(f"s_add_u32 s{r}, %[{kind}lo], s{S_SOFF}")
+    emit(f"s_addc_u32 s{r + 1}, %[{kind}hi], 0")
+    emit(f"s_sub_u32 s{r + 2}, %[hb], s{S_SOFF}")
+    emit(f"s_cselect_b32 s{r + 2}, 0, s{r + 2}")
+    emit(f"s_mov_b32 s{r + 3}, 0x20000")
+
+
+def dma_groups(kind, dst_off, r):
     """Buffer->LDS loads of one K or V tile as instruction groups: this
     wavefront's 1 KiB blocks wave, wave + 4, ...; block 16 belongs to
     wavefront 0, so the other wavefronts issue that load with no lane active
-    (EXEC = 0: nothing is read or written).  The source offset of the tile is
-    in s[soff_sgpr]."""
-    rs = "%[krsrc]" if kind == "k" else "%[vrsrc]"
+    (EXEC = 0: nothing is read or written).  The tile's resource is in
+    s[r:r+3]."""
+    rs = f"s[{r}:{r + 3}]"
     out = []
     for p in range((LOADS + WAVES - 1) // WAVES):
         g = []
@@ -343,25 +362,25 @@ def dma_groups(kind, dst_off, soff_sgpr):
         if partial:
             g += ["s_cmp_eq_u32 %[wave], 0", "s_cselect_b64 exec, -1, 0", "s_nop 4"]
         g += [f"s_add_u32 m0, %[wbase], {dst_off + p * WAVES * 1024}", "s_nop 1",
-              f"buffer_load_dwordx4 %[{kind}vo{p}], {rs}, s{soff_sgpr} offen lds"]
+              f"buffer_load_dwordx4 %[{kind}vo{p}], {rs}, 0 offen lds"]
         if partial:
             g += ["s_mov_b64 exec, -1", "s_nop 4"]
         out.append(g)
     return out
 
 
-def dma_tile(st, kind, dst_off, tile_sgpr_expr, label):
+def dma_tile(st, kind, dst_off, tile_sgpr, label):
     """Buffer->LDS loads of one K or V tile: this wavefront's 1 KiB blocks
     wave, wave + 4, ... (block 16 only on wavefront 0)."""
-    st.emit(f"s_lshl_b32 s{S_SOFF}, {tile_sgpr_expr}, {14}")
+    r = S_RK if kind == "k" else S_RV
+    tile_rsrc(st.emit, kind, tile_sgpr, r)
     for p in range((LOADS + WAVES - 1) // WAVES):
         if WAVES * p + WAVES > LOADS:
             st.emit("s_cmp_lg_u32 %[wave], 0")
             st.emit(f"s_cbranch_scc1 {label}_%=")
         st.emit(f"s_add_u32 m0, %[wbase], {dst_off + p * WAVES * 1024}")
         st.emit("s_nop 1")
-        rs = "%[krsrc]" if kind == "k" else "%[vrsrc]"
-        st.emit(f"buffer_load_dwordx4 %[{kind}vo{p}], {rs}, s{S_SOFF} offen lds")
+        st.emit(f"buffer_load_dwordx4 %[{kind}vo{p}], s[{r}:{r + 3}], 0 offen lds")
     st.emit(f"{label}_%=:")
 
 
@@ -437,14 +456,14 @@ def step(st, parity, causal, kind, label):
     groups = []
     if kind in ("full", "first"):
         # K_{j+2} into K buffer j & 1, last read in step j-1.  Past the last
-        # tile it reads zeros (or unneeded keys) into a buffer nobody reads.
+        # tile its resource is empty: zeros into a buffer nobody reads.
         st.emit(f"s_add_u32 s{S_T2}, s{S_J}, 2")
-        st.emit(f"s_lshl_b32 s{S_SOFF}, s{S_T2}, 14")
-        groups += dma_groups("k", KV_LDS[j_odd], S_SOFF)
+        tile_rsrc(st.emit, "k", S_T2, S_RK)
+        groups += dma_groups("k", KV_LDS[j_odd], S_RK)
     if kind in ("full", "last"):
         # V_j into V buffer j & 1, last read (V_{j-2}) in step j-1
-        st.emit(f"s_lshl_b32 s{S_SOFFV}, s{S_J}, 14")
-        groups += dma_groups("v", KV_LDS[2 + j_odd], S_SOFFV)
+        tile_rsrc(st.emit, "v", S_J, S_RV)
+        groups += dma_groups("v", KV_LDS[2 + j_odd], S_RV)
     mask_block(st, j_odd, causal, f"{label}_mask")
     valu = softmax_ops(j_odd, j_odd, fast=(kind != "first"))
     if kind == "full":
@@ -489,19 +508,20 @@ def item_asm(causal):
     e(f"v_mov_b32 v{V_L[1]}, 0")
     for k in range(128):
         e(f"v_accvgpr_write_b32 a{k}, 0")
-    # Q fragments into AGPRs (rows past N read as zeros)
-    e(f"s_movk_i32 s{S_Q1}, 0x2000")
+    # Q fragments into AGPRs (rows past N read as zeros); query block 1 is
+    # 32 rows (8 KiB) further
+    e(f"v_add_u32 v{TMP0}, 0x2000, %[qvo]")
     for qb in range(2):
         for ds in range(8):
             q = 128 + (8 * qb + ds) * 4
-            so = "0" if qb == 0 else f"s{S_Q1}"
-            e(f"buffer_load_dwordx4 a[{q}:{q + 3}], %[qvo], %[qrsrc], {so} offen offset:{32 * ds}")
+            vo = "%[qvo]" if qb == 0 else f"v{TMP0}"
+            e(f"buffer_load_dwordx4 a[{q}:{q + 3}], {vo}, %[qrsrc], 0 offen offset:{32 * ds}")
     # K_0, V_0, K_1
     e(f"s_mov_b32 s{S_J}, 0")
-    dma_tile(st, "k", KV_LDS[0], f"s{S_J}", "pk0")
-    dma_tile(st, "v", KV_LDS[2], f"s{S_J}", "pv0")
+    dma_tile(st, "k", KV_LDS[0], S_J, "pk0")
+    dma_tile(st, "v", KV_LDS[2], S_J, "pv0")
     e(f"s_mov_b32 s{S_T2}, 1")
-    dma_tile(st, "k", KV_LDS[1], f"s{S_T2}", "pk1")
+    dma_tile(st, "k", KV_LDS[1], S_T2, "pk1")
     e("s_waitcnt vmcnt(0)")
     e("s_barrier")
     # S_0 = K_0 Q^T
