@@ -263,7 +263,7 @@ int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* L, int B
   int cus = 0;
   if ((st = cu_count(&cus)) != FA_OK) return st;
   fa::FwdArgs a{Q, K, V, O, L, B, H, N, causal, scale,
-                (int)fa::fwd_grid(fa::fwd_units(B, H, N, causal), causal, cus)};
+                (int)fa::fwd_grid(fa::fwd_units(B, H, N, causal), d, causal, cus)};
   hipError_t e = fa::launch_fwd_bf16(a, d, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "fa_fwd launch");
   return ok();
@@ -290,9 +290,9 @@ int fa_fwd_plan(int B, int H, int N, int d, int causal, fa_fwd_plan_t* out) {
   out->q_tiles = q_tiles;
   out->kv_tiles = (int)fa::ceil_div64(N, fa::kFwdBC);
   out->threads_per_workgroup = fa::fwd_threads(d, causal);
-  out->lds_bytes = fa::fwd_lds_bytes(d);
+  out->lds_bytes = fa::fwd_lds_for(d, causal);
   out->work_units = fa::fwd_units(B, H, N, causal);
-  out->workgroups = fa::fwd_grid(out->work_units, causal, kPlanCUs);
+  out->workgroups = fa::fwd_grid(out->work_units, d, causal, kPlanCUs);
   int64_t visited = 0, masked = 0;
   for (int qt = 0; qt < q_tiles; ++qt) {
     const int n = fa::fwd_kv_tiles_for(qt, N, causal);

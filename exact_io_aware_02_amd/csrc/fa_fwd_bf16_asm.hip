@@ -22,6 +22,11 @@
 //    and two probability tiles in VGPRs.  The compiler cannot hold that many
 //    values without spilling, so one query tile's loop is assembly generated
 //    by gen_fwd_asm.py with one fixed register for every value.
+//  * Persistent workgroups, one per compute unit: during an item's last
+//    product block the next item's Q fragments and first two K tiles load
+//    into the registers and K buffers that block no longer reads, and the
+//    output leaves through a staging area of its own, so consecutive items
+//    do not wait for each other's loads or stores.
 
 #include "fa_device.h"
 #include "fa_internal.h"
@@ -39,14 +44,17 @@ constexpr int kBR = 64 * kWaves;
 constexpr int kBC = 64;
 constexpr int kStride = 2 * D + 16;
 constexpr int kTile = kBC * kStride;
-constexpr int kLds = 4 * kTile;
+// [K buffer 0][K buffer 1][V buffer 0][V buffer 1][output staging: 64 rows
+// per wavefront]; one workgroup fills a compute unit (160 KiB of LDS)
+constexpr int kKV = 4 * kTile;
+constexpr int kLds = kKV + kWaves * 64 * kStride;
 static_assert(kBR == kFwdBR && kBC == kFwdBC, "tiles must match the planner");
-static_assert(kLds == fwd_lds_bytes(D), "LDS size must match the planner");
+static_assert(kKV == fwd_lds_bytes(D) && kLds == fwd_asm_lds_bytes(), "LDS size must match the planner");
 
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void fwd_bf16_asm_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ Kg,
                          const __bf16* __restrict__ Vg, __bf16* __restrict__ Og,
-                         float* __restrict__ Lg, int N, int q_tiles, float scale) {
+                         float* __restrict__ Lg, int N, int q_tiles, int items, float scale) {
   __shared__ __attribute__((aligned(1024))) char smem[kLds];
   char LDS_AS* lds = (char LDS_AS*)smem;
   const unsigned lds_base = (unsigned)(size_t)lds;
@@ -65,82 +73,92 @@ void fwd_bf16_asm_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict
     kvo[p] = padded_source<D>(o, false);
     vvo[p] = padded_source<D>(o, true);
   }
-  // LDS read bases: K fragments, transposing V reads (V buffers start after
-  // the two K buffers), this wavefront's 64 output staging rows
+  // LDS bases: K fragments, transposing V reads (V buffers start after the
+  // two K buffers), this wavefront's 64 staging rows as written from the
+  // accumulators (row l32 of a query block, 8 columns per lane group) and as
+  // read for the stores (row lane / 16 + 4 k, 16 bytes at lane % 16)
   const unsigned kb = lds_base + l32 * kStride + g * 16;
   const unsigned vb = lds_base + 2 * kTile + tr_lane_base<kStride>(lane);
-  const unsigned stg = lds_base + wave * 64 * kStride + l32 * kStride + 8 * g;
+  const unsigned stage = lds_base + kKV + wave * 64 * kStride;
+  const unsigned stg = stage + l32 * kStride + 8 * g;
+  const unsigned srd = stage + (lane >> 4) * kStride + (lane & 15) * 16;
   const unsigned wbase = lds_base + wave * 1024;
 
   const float c = scale * kLog2e;
   const float theta = 8.f / c;  // conditional-rescale threshold, raw score units
   const unsigned head_bytes = (unsigned)N * D * 2;
+  const int n = (N + kBC - 1) / kBC;
+  // keys past N are masked: the loop compares key - 4 g against N - 1 - 4 g
+  const int limg = N - 1 - 4 * g;
 
-
-  // one query tile: the generated loop, then O and L of this wavefront's rows
-  auto item = [&](const int bh, const int qt) {
-    const size_t head_off = (size_t)bh * N * D;
-    const int qw0 = __builtin_amdgcn_readfirstlane(qt * kBR + wave * 64);
-    const int n = (N + kBC - 1) / kBC;
-    const u32x4_t q_rsrc = make_rsrc(Qg + head_off, head_bytes);
-    // K and V head bases: the loop builds each tile's resource from them
-    const unsigned long long ka = (unsigned long long)(Kg + head_off);
-    const unsigned long long va = (unsigned long long)(Vg + head_off);
-    const unsigned klo = (unsigned)ka, khi = (unsigned)(ka >> 32) & 0xFFFFu;
-    const unsigned vlo = (unsigned)va, vhi = (unsigned)(va >> 32) & 0xFFFFu;
-    const unsigned qvo = (unsigned)(qw0 + l32) * D * 2 + g * 16;
-    // keys past N are masked: the loop compares key - 4 g against N - 1 - 4 g
-    const int limg = N - 1 - 4 * g;
-    float mo0, mo1, lo0, lo1;
-    asm volatile(FA_ASM_ITEM
-                 : [mo0] "=v"(mo0), [mo1] "=v"(mo1), [lo0] "=v"(lo0), [lo1] "=v"(lo1)
-                 : [kvo0] "v"(kvo[0]), [kvo1] "v"(kvo[1]), [kvo2] "v"(kvo[2]), [kvo3] "v"(kvo[3]),
-                   [kvo4] "v"(kvo[4]), [vvo0] "v"(vvo[0]), [vvo1] "v"(vvo[1]), [vvo2] "v"(vvo[2]),
-                   [vvo3] "v"(vvo[3]), [vvo4] "v"(vvo[4]), [qvo] "v"(qvo), [kb] "v"(kb), [vb] "v"(vb),
-                   [stg] "v"(stg), [limg0] "v"(limg), [limg1] "v"(limg), [qrsrc] "s"(q_rsrc),
-                   [klo] "s"(klo), [khi] "s"(khi), [vlo] "s"(vlo), [vhi] "s"(vhi), [hb] "s"(head_bytes),
-                   [n] "s"(n), [c] "v"(c), [theta] "v"(theta),
-                   [wave] "s"(wave), [wbase] "s"(wbase), [n_keys] "s"(N), [qw0] "s"(qw0)
-                 : FA_ASM_CLOBBERS);
-    // the wavefront's 64 rows of O wait in its staging rows (written and
-    // waited for by the loop): whole rows leave with one 16-byte store per
-    // lane, 16 lanes per 256-byte row
-    const char LDS_AS* stage = lds + wave * 64 * kStride;
-    const int rr = lane >> 4, ch = lane & 15;
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const int r = 4 * k + rr;
-      const u32x4_t v = *(const u32x4_t LDS_AS*)(stage + r * kStride + ch * 16);
-      if (qw0 + r < N) *reinterpret_cast<u32x4_t*>(Og + head_off + (size_t)(qw0 + r) * D + ch * 8) = v;
-    }
-    if (Lg != nullptr && g == 0) {
-      if (qw0 + l32 < N) Lg[(size_t)bh * N + qw0 + l32] = mo0 * scale + __logf(lo0);
-      if (qw0 + 32 + l32 < N) Lg[(size_t)bh * N + qw0 + 32 + l32] = mo1 * scale + __logf(lo1);
-    }
-    // every wavefront has read its rows back before the next item's loads
-    // reuse the area
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    wg_barrier();
-  };
-
-  // one workgroup per query tile; workgroup ids are remapped so that the
-  // query tiles running at once on an XCD (dispatch is round-robin over the 8
-  // XCDs) belong to the same heads and share their K/V in that XCD's L2
+  // persistent: G workgroups take items lw, lw + G, ... (lw: the workgroup's
+  // logical index).  Dispatch is round-robin over the 8 XCDs and lw places a
+  // contiguous run of workgroups on one XCD, so the items running at once on
+  // an XCD are consecutive query tiles of the same heads and share K/V in
+  // that XCD's L2.
   const int G = gridDim.x;
   const int wg = blockIdx.x;
   const int per = G >> 3, rem = G & 7;
   const int xcd = wg & 7, slot_id = wg >> 3;
-  const int logical = xcd * per + (xcd < rem ? xcd : rem) + slot_id;
-  const int bh = logical / q_tiles;
-  item(bh, logical - bh * q_tiles);
+  const int lw = xcd * per + (xcd < rem ? xcd : rem) + slot_id;
+
+  int it = lw;
+  int pre = 0;
+  while (it < items) {
+    const int bh = it / q_tiles;
+    const int qt = it - bh * q_tiles;
+    const int nit = it + G;
+    const bool more = nit < items;
+    const int nbh = more ? nit / q_tiles : bh;
+    const int nqt = more ? nit - nbh * q_tiles : qt;
+
+    const size_t head_off = (size_t)bh * N * D;
+    const size_t nhead_off = (size_t)nbh * N * D;
+    const int qw0 = __builtin_amdgcn_readfirstlane(qt * kBR + wave * 64);
+    const int nqw0 = nqt * kBR + wave * 64;
+    const u32x4_t q_rsrc = make_rsrc(Qg + head_off, head_bytes);
+    const u32x4_t nq_rsrc = make_rsrc(Qg + nhead_off, more ? head_bytes : 0u);
+    const u32x4_t o_rsrc = make_rsrc(Og + head_off, head_bytes);
+    const u32x4_t l_rsrc = Lg != nullptr ? make_rsrc(Lg + (size_t)bh * N, (unsigned)N * 4) : make_rsrc(nullptr, 0u);
+    // K and V head bases: the loop builds each tile's resource from them
+    const unsigned long long ka = (unsigned long long)(Kg + head_off);
+    const unsigned long long va = (unsigned long long)(Vg + head_off);
+    const unsigned long long nka = (unsigned long long)(Kg + nhead_off);
+    const unsigned klo = (unsigned)ka, khi = (unsigned)(ka >> 32) & 0xFFFFu;
+    const unsigned vlo = (unsigned)va, vhi = (unsigned)(va >> 32) & 0xFFFFu;
+    const unsigned nklo = (unsigned)nka, nkhi = (unsigned)(nka >> 32) & 0xFFFFu;
+    const unsigned nhb = more ? head_bytes : 0u;
+    const unsigned qvo = (unsigned)(qw0 + l32) * D * 2 + g * 16;
+    const unsigned nqvo = (unsigned)(nqw0 + l32) * D * 2 + g * 16;
+    const unsigned ovo = (unsigned)(qw0 + (lane >> 4)) * D * 2 + (lane & 15) * 16;
+    const unsigned lvo = (unsigned)(qw0 + l32) * 4;
+    asm volatile(FA_ASM_ITEM
+                 :
+                 : [kvo0] "v"(kvo[0]), [kvo1] "v"(kvo[1]), [kvo2] "v"(kvo[2]), [kvo3] "v"(kvo[3]),
+                   [kvo4] "v"(kvo[4]), [vvo0] "v"(vvo[0]), [vvo1] "v"(vvo[1]), [vvo2] "v"(vvo[2]),
+                   [vvo3] "v"(vvo[3]), [vvo4] "v"(vvo[4]), [qvo] "v"(qvo), [nqvo] "v"(nqvo), [kb] "v"(kb),
+                   [vb] "v"(vb), [stg] "v"(stg), [srd] "v"(srd), [ovo] "v"(ovo), [lvo] "v"(lvo),
+                   [limg0] "v"(limg), [limg1] "v"(limg), [c] "v"(c), [theta] "v"(theta),
+                   [qrsrc] "s"(q_rsrc), [nqrsrc] "s"(nq_rsrc), [orsrc] "s"(o_rsrc), [lrsrc] "s"(l_rsrc),
+                   [klo] "s"(klo), [khi] "s"(khi), [vlo] "s"(vlo), [vhi] "s"(vhi), [hb] "s"(head_bytes),
+                   [nklo] "s"(nklo), [nkhi] "s"(nkhi), [nhb] "s"(nhb), [n] "s"(n), [wave] "s"(wave),
+                   [wbase] "s"(wbase), [n_keys] "s"(N), [qw0] "s"(qw0), [pre] "s"(pre)
+                 : FA_ASM_CLOBBERS);
+    pre = 1;
+    it = nit;
+  }
+  // the last item's stores (and its empty prefetch) complete before the
+  // workgroup's LDS and registers are released
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 hipError_t launch(const FwdArgs& a, hipStream_t stream) {
   const int q_tiles = (a.N + kBR - 1) / kBR;
+  const int64_t items = (int64_t)a.B * a.H * q_tiles;
   hipLaunchKernelGGL(fwd_bf16_asm_kernel, dim3((unsigned)a.grid), dim3(kThreads), 0, stream,
                      static_cast<const __bf16*>(a.Q), static_cast<const __bf16*>(a.K),
                      static_cast<const __bf16*>(a.V), static_cast<__bf16*>(a.O), a.L, a.N, q_tiles,
-                     a.scale);
+                     (int)items, a.scale);
   return hipGetLastError();
 }
 

@@ -19,6 +19,9 @@ constexpr int kFwdBC = FA_FWD_BC;
 // LDS of one prefill workgroup: two K and two V tiles, each row padded by 16
 // bytes (the query tile lives in registers).
 __host__ __device__ constexpr int fwd_lds_bytes(int d) { return 4 * kFwdBC * (2 * d + 16); }
+// LDS of the d = 128 kernel with generated assembly: the same K/V buffers
+// plus 256 padded output staging rows.
+__host__ __device__ constexpr int fwd_asm_lds_bytes() { return fwd_lds_bytes(128) + 256 * (2 * 128 + 16); }
 
 // fp32 prefill: one wavefront, one query row per lane, 64-key tiles.
 constexpr int kF32BR = 64;
@@ -101,6 +104,7 @@ struct DecodeArgs {
 // every other bf16 prefill the 32-rows-per-wavefront one (8 wavefronts).
 // Both use the tiles above.
 inline bool fwd_uses_asm(int d, int causal) { return d == 128 && !causal; }
+inline int fwd_lds_for(int d, int causal) { return fwd_uses_asm(d, causal) ? fwd_asm_lds_bytes() : fwd_lds_bytes(d); }
 inline int fwd_threads(int d, int causal) { return fwd_uses_asm(d, causal) ? 4 * 64 : kFwdWaves * 64; }
 
 // Launchers: enqueue on `stream`, return hipGetLastError().
@@ -130,13 +134,15 @@ inline int64_t fwd_units(int B, int H, int N, int causal) {
   const int64_t q_tiles = ceil_div64(N, kFwdBR);
   return (int64_t)B * H * (causal ? (q_tiles + 1) / 2 : q_tiles);
 }
-// Grid of the bf16 prefill.  Causal: persistent, one workgroup per compute
-// unit (fewer if there are fewer units), each taking every grid-th pair of
-// query tiles, so that all workgroups get the same work.  Non-causal: every
-// unit already has the same work, and one workgroup per unit lets the
+// Grid of the bf16 prefill.  Persistent, one workgroup per compute unit
+// (fewer if there are fewer units), each taking every grid-th unit: always
+// for causal attention (pairs of query tiles, so all workgroups get the same
+// work) and for the kernel with generated assembly (whose items prefetch
+// their successor's loads).  Otherwise one workgroup per unit, which lets the
 // hardware overlap one workgroup's start with another's end.
-inline int64_t fwd_grid(int64_t units, int causal, int cus) {
-  return causal ? (units < cus ? units : cus) : units;
+inline int64_t fwd_grid(int64_t units, int d, int causal, int cus) {
+  const bool persistent = causal || fwd_uses_asm(d, causal);
+  return persistent ? (units < cus ? units : cus) : units;
 }
 
 // Blocks a chunk of at most chunk_tokens tokens can touch when chunks start

@@ -6,8 +6,11 @@ FlashAttention forward (64 query rows per wavefront, one wavefront per SIMD).
 The build runs this before compiling fa_fwd_bf16_asm.hip, which includes the
 output: the C string macro FA_ASM_ITEM, the body of one inline-asm statement
 that runs Algorithm 1 of "Infra: Flash Attention" ("Tiled computation and
-forward") without a causal mask for one query tile of a wavefront and leaves
-O = U / l, as bf16 rows, in LDS (keys past N are masked).
+forward") without a causal mask for one query tile of a wavefront and stores
+its rows of O = U / l (bf16) and L = m + log l (keys past N are masked).
+While its last product block runs, an item loads the next item's Q, K_0 and
+K_1, so a persistent workgroup's items follow one another with no wait for
+those loads.
 
 Why assembly: a wavefront keeps U^T for 64 queries (128 AGPRs), its Q
 fragments (64 AGPRs), two score tiles and two probability tiles (192 VGPRs)
@@ -450,8 +453,10 @@ def step(st, parity, causal, kind, label):
     QK of j+1, softmax of j), 'last' (PV of j-1, softmax of j), 'first'
     (j = 0: QK of 1, softmax of 0)."""
     j_odd = parity
-    # top: own loads landed, every wavefront done with step j-1's buffers
-    st.emit("s_waitcnt vmcnt(0) lgkmcnt(0)")
+    # top: own loads landed, every wavefront done with step j-1's buffers.
+    # Step 0 reads only K_1, waited for before S_0; V_0 (and the previous
+    # item's stores) are left to step 1's wait.
+    st.emit("s_waitcnt lgkmcnt(0)" if kind == "first" else "s_waitcnt vmcnt(0) lgkmcnt(0)")
     st.emit("s_barrier")
     groups = []
     if kind in ("full", "first"):
@@ -494,7 +499,48 @@ def step(st, parity, causal, kind, label):
         st.emit(f"{label}_done_%=:")
 
 
+LN2 = "0x3f317218"           # ln 2 as fp32
+
+
+def prefetch_groups():
+    """The next item's K_0, K_1 (into K buffers 0, 1) and Q fragments (into
+    a[128:191]) as load groups; the caller has set up their resources."""
+    q = []
+    for qb in range(2):
+        for ds in range(8):
+            f = 128 + (8 * qb + ds) * 4
+            vo = "%[nqvo]" if qb == 0 else f"v{TMP0 + 15}"
+            q.append(f"buffer_load_dwordx4 a[{f}:{f + 3}], {vo}, %[nqrsrc], 0 offen offset:{32 * ds}")
+    qg = [q[i:i + 2] for i in range(0, 16, 2)]
+    return (dma_groups("k", KV_LDS[0], S_RK) + qg[:4] + dma_groups("k", KV_LDS[1], S_RV) + qg[4:])
+
+
+def prefetch_setup(e):
+    """Resources of the next item's K_0 and K_1 (empty if there is none:
+    %[nhb] = 0) and the VGPR offset of its second query block."""
+    e(f"v_add_u32 v{TMP0 + 15}, 0x2000, %[nqvo]")
+    for t, r in ((0, S_RK), (1, S_RV)):
+        e(f"s_mov_b32 s{S_T2}, {t}")
+        e(f"s_lshl_b32 s{S_SOFF}, s{S_T2}, 14")
+        e(f"s_add_u32 s{r}, %[nklo], s{S_SOFF}")
+        e(f"s_addc_u32 s{r + 1}, %[nkhi], 0")
+        e(f"s_sub_u32 s{r + 2}, %[nhb], s{S_SOFF}")
+        e(f"s_cselect_b32 s{r + 2}, 0, s{r + 2}")
+        e(f"s_mov_b32 s{r + 3}, 0x20000")
+
+
+# VMEM instructions a wavefront issues between the prefetch of the next
+# item's Q, K_0, K_1 and that item's wait for them: the 16 O-row stores and
+# 2 L stores of this item, then the next item's V_0 loads (4 or 5: whether
+# a load with no lane active counts is not relied on, so 4)
+VM_AFTER_PREFETCH = 16 + 2 + 4
+
+
 def item_asm(causal):
+    """One query tile of a wavefront: the tile loop, then O and L stored.
+    %[pre] = 1: Q, K_0, K_1 were prefetched by the previous item, which
+    issued nothing but its stores after them.  Every item prefetches those of
+    the next one (%[nq*], %[nk*]; empty resources if there is none)."""
     st = Stream()
     e = st.emit
     e(f"s_mov_b32 s{S_M0}, m0")
@@ -506,26 +552,44 @@ def item_asm(causal):
     e(f"v_mov_b32 v{V_M[1]}, 0xff800000")
     e(f"v_mov_b32 v{V_L[0]}, 0")
     e(f"v_mov_b32 v{V_L[1]}, 0")
-    for k in range(128):
-        e(f"v_accvgpr_write_b32 a{k}, 0")
-    # Q fragments into AGPRs (rows past N read as zeros); query block 1 is
-    # 32 rows (8 KiB) further
+    # the first item of a workgroup loads Q (rows past N read as zeros; query
+    # block 1 is 32 rows, 8 KiB, further), K_0 and K_1 itself
+    e("s_cmp_eq_u32 %[pre], 0")
+    e("s_cbranch_scc0 L_pre_%=")
     e(f"v_add_u32 v{TMP0}, 0x2000, %[qvo]")
     for qb in range(2):
         for ds in range(8):
             q = 128 + (8 * qb + ds) * 4
             vo = "%[qvo]" if qb == 0 else f"v{TMP0}"
             e(f"buffer_load_dwordx4 a[{q}:{q + 3}], {vo}, %[qrsrc], 0 offen offset:{32 * ds}")
-    # K_0, V_0, K_1
-    e(f"s_mov_b32 s{S_J}, 0")
-    dma_tile(st, "k", KV_LDS[0], S_J, "pk0")
-    dma_tile(st, "v", KV_LDS[2], S_J, "pv0")
+    e(f"s_mov_b32 s{S_T2}, 0")
+    tile_rsrc(e, "k", S_T2, S_RK)
+    for g in dma_groups("k", KV_LDS[0], S_RK):
+        for ins in g:
+            e(ins)
     e(f"s_mov_b32 s{S_T2}, 1")
-    dma_tile(st, "k", KV_LDS[1], S_T2, "pk1")
-    e("s_waitcnt vmcnt(0)")
+    tile_rsrc(e, "k", S_T2, S_RK)
+    for g in dma_groups("k", KV_LDS[1], S_RK):
+        for ins in g:
+            e(ins)
+    e("L_pre_%=:")
+    # V_0
+    e(f"s_mov_b32 s{S_J}, 0")
+    tile_rsrc(e, "v", S_J, S_RV)
+    for g in dma_groups("v", KV_LDS[2], S_RV):
+        for ins in g:
+            e(ins)
+    # wait for Q, K_0, K_1 (not V_0, nor the previous item's stores)
+    e("s_cmp_eq_u32 %[pre], 0")
+    e("s_cbranch_scc0 L_prew_%=")
+    e("s_waitcnt vmcnt(4)")
+    e("s_branch L_prewd_%=")
+    e("L_prew_%=:")
+    e(f"s_waitcnt vmcnt({VM_AFTER_PREFETCH})")
+    e("L_prewd_%=:")
     e("s_barrier")
-    # S_0 = K_0 Q^T
-    st.block(qk_frags(0, 0), [])
+    # S_0 = K_0 Q^T, U = 0 alongside
+    st.block(qk_frags(0, 0), [f"v_accvgpr_write_b32 a{k}, 0" for k in range(128)])
     e("s_nop 15")
     e("s_nop 15")
     # step 0
@@ -546,21 +610,26 @@ def item_asm(causal):
     e(f"s_add_u32 s{S_J}, s{S_J}, 1")
     e("s_branch L_loop_%=")
     # last step j = n - 1 (odd), then U += V_{n-1} W_{n-1} from buffers 1
+    # while the next item's Q, K_0, K_1 load (no K buffer and no Q fragment
+    # is read after step n - 2)
     e("L_last1_%=:")
     step(st, 1, causal, "last", "sl1")
     e("s_waitcnt vmcnt(0) lgkmcnt(0)")
     e("s_barrier")
-    st.block(pv_frags(1, 1), [])
+    prefetch_setup(e)
+    st.block(pv_frags(1, 1), [], groups=prefetch_groups())
     e("s_branch L_done_%=")
     e("L_last0_%=:")
     step(st, 0, causal, "last", "sl0")
     e("L_fin0_%=:")
     e("s_waitcnt vmcnt(0) lgkmcnt(0)")
     e("s_barrier")
-    st.block(pv_frags(0, 0), [])
+    prefetch_setup(e)
+    st.block(pv_frags(0, 0), [], groups=prefetch_groups())
     e("L_done_%=:")
-    # epilogue: every wavefront done with the K/V area; O = U / l into this
-    # wavefront's 64 staging rows (l summed over the lane pair first)
+    # epilogue: every wavefront done with the V buffers (the next item loads
+    # V_0 at once); O = U / l into this wavefront's 64 staging rows (l summed
+    # over the lane pair first)
     e("s_waitcnt lgkmcnt(0)")
     e("s_barrier")
     for qb in range(2):
@@ -584,11 +653,29 @@ def item_asm(causal):
                 e(f"v_cvt_pk_bf16_f32 v{TMP0 + 5}, v{TMP0 + 2}, v{TMP0 + 3}")
                 off = qb * 32 * STRIDE + 64 * db + 16 * i4
                 e(f"ds_write_b64 %[stg], v[{TMP0 + 4}:{TMP0 + 5}] offset:{off}")
+    # L = ln l + m scale = (log2 l + c m) ln 2, for rows qw0 + l32 and
+    # qw0 + 32 + l32 (both lanes of a pair store the same value)
+    for qb in range(2):
+        e(f"v_log_f32 v{TMP0 + 8 + qb}, v{V_L[qb]}")
+    e(f"v_add_u32 v{TMP0 + 12}, 0x1000, %[ovo]")
+    for qb in range(2):
+        e(f"v_add_f32 v{TMP0 + 8 + qb}, v{TMP0 + 8 + qb}, v{V_MC[qb]}")
+    e(f"v_add_u32 v{TMP0 + 13}, 0x2000, %[ovo]")
+    for qb in range(2):
+        e(f"v_mul_f32 v{TMP0 + 8 + qb}, {LN2}, v{TMP0 + 8 + qb}")
+    e(f"v_add_u32 v{TMP0 + 14}, 0x3000, %[ovo]")
+    # the wavefront's 64 rows leave whole: lane (r, ch) = (lane / 16, lane %
+    # 16) reads 16 bytes of rows 4 k + r and stores them (rows past N are
+    # past the resource's end: dropped)
     e("s_waitcnt lgkmcnt(0)")
-    e(f"v_mov_b32 %[mo0], v{V_M[0]}")
-    e(f"v_mov_b32 %[mo1], v{V_M[1]}")
-    e(f"v_mov_b32 %[lo0], v{V_L[0]}")
-    e(f"v_mov_b32 %[lo1], v{V_L[1]}")
+    for k in range(16):
+        e(f"ds_read_b128 v[{4 * k}:{4 * k + 3}], %[srd] offset:{4 * k * STRIDE}")
+    e("s_waitcnt lgkmcnt(0)")
+    for k in range(16):
+        vo = "%[ovo]" if k < 4 else f"v{TMP0 + 11 + k // 4}"
+        e(f"buffer_store_dwordx4 v[{4 * k}:{4 * k + 3}], {vo}, %[orsrc], 0 offen offset:{1024 * (k % 4)}")
+    e(f"buffer_store_dword v{TMP0 + 8}, %[lvo], %[lrsrc], 0 offen")
+    e(f"buffer_store_dword v{TMP0 + 9}, %[lvo], %[lrsrc], 0 offen offset:128")
     e(f"s_mov_b32 m0, s{S_M0}")
     return st.out
 

@@ -171,9 +171,13 @@ def test_fwd_plan_tile_count_matches_oracle(N, causal):
     assert p["tiles_visited"] == 6 * cnt["tiles"]
     q_tiles = -(-N // p["block_rows"])
     assert p["q_tiles"] == q_tiles
-    # persistent grid over work units: query tiles, or causal pairs of them
+    # persistent grid over work units (query tiles, or causal pairs of them),
+    # one workgroup per compute unit at most: at d = 128 both kernels are
+    # persistent
     assert p["work_units"] == 6 * (-(-q_tiles // 2) if causal else q_tiles)
-    assert p["workgroups"] == (min(p["work_units"], 256) if causal else p["work_units"])
+    assert p["workgroups"] == min(p["work_units"], 256)
+    p64 = fa.fa_fwd_plan(2, 3, N, 64, causal)
+    assert p64["workgroups"] == (min(p64["work_units"], 256) if causal else p64["work_units"])
 
 
 def test_fwd_plan_causal_pin_exercise4():

@@ -60,7 +60,7 @@ def _parse(line):
     op, _, rest = line.partition(" ")
     args = [a.strip() for a in rest.split(",")] if rest else []
     no_dst = op.startswith(("s_cmp", "s_cbranch", "s_branch", "s_waitcnt", "s_nop", "s_barrier",
-                            "ds_write", "s_setprio"))
+                            "ds_write", "s_setprio", "buffer_store"))
     if op.startswith("buffer_load") and rest.endswith("lds"):
         no_dst = True
     if no_dst or not args:
@@ -243,6 +243,28 @@ def test_every_exec_change_is_undone_before_vector_work(program):
             continue
         if masked:
             assert op.startswith(("s_", "buffer_load")), f"vector work with EXEC changed: {line}"
+
+
+def test_prefetch_wait_counts_only_later_instructions(program):
+    """An item waits for the loads its predecessor prefetched with
+    s_waitcnt vmcnt(k), where k is the number of VMEM instructions issued
+    after them (vmcnt falls in issue order): the predecessor's stores after
+    its last prefetch load, plus this item's V_0 loads before the wait,
+    counting a load with no lane active as issued or not."""
+    g, prog = program
+    last = max(i for i, ln in enumerate(prog) if ln.startswith("buffer_load"))
+    assert "%[nqrsrc]" in prog[last] or "%[nklo]" in "".join(prog[last - 40:last])
+    stores = sum(1 for ln in prog[last + 1:] if ln.startswith("buffer_store"))
+    assert not any(ln.startswith("buffer_load") for ln in prog[last + 1:])
+    a = prog.index("L_pre_%=:")
+    b = next(i for i in range(a, len(prog)) if prog[i].startswith("s_waitcnt vmcnt("))
+    v0 = [ln for ln in prog[a:b] if ln.startswith("buffer_load")]
+    masked = sum(1 for i in range(a, b) if prog[i].startswith("s_cselect_b64 exec"))
+    assert stores == 18 and len(v0) == 5 and masked == 1
+    assert g.VM_AFTER_PREFETCH == stores + len(v0) - masked
+    assert f"s_waitcnt vmcnt({g.VM_AFTER_PREFETCH})" in prog
+    # the first item of a workgroup waits for all but V_0 (4 or 5 loads)
+    assert "s_waitcnt vmcnt(4)" in prog
 
 
 def test_generator_output_is_deterministic(tmp_path):
