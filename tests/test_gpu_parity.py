@@ -161,24 +161,31 @@ def test_bf16_ragged_tail_reads_nothing_past_the_head(N, d):
         assert dO <= BF16_O and dL <= BF16_L, (causal, dO, dL)
 
 
-@pytest.mark.parametrize("B,H,N", [(2, 200, 50), (1, 300, 300), (1, 520, 129), (3, 100, 700)])
-def test_bf16_causal_many_items_per_workgroup(B, H, N):
-    """Causal launches keep at most one workgroup per compute unit, so with
-    many heads each workgroup runs a sequence of query tiles, staging the
-    next tile's Q and first K/V tiles during the current one and storing the
-    previous tile's output inside the next.  Covers single-tile items (N <=
-    64: every step is an item boundary) and mixes of long and short items;
-    every head and row is compared."""
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("B,H,N", [(2, 200, 50), (1, 300, 300), (1, 520, 129), (3, 100, 700),
+                                   (1, 257, 513)])
+def test_bf16_many_items_per_workgroup(B, H, N, causal):
+    """At d = 128 launches keep at most one workgroup per compute unit, so
+    with many heads each workgroup runs a sequence of query tiles whose heads
+    change from one to the next.  Causal: the next tile's Q and first K/V
+    tiles are staged during the current one and the previous tile's output
+    is stored inside the next.  Non-causal: an item's last product block
+    loads the next item's Q, K_0 and K_1, and the next item waits for them
+    behind the previous item's stores.  Covers single-tile items (N <= 64:
+    every step is an item boundary), ragged last tiles, a grid with fewer
+    items than compute units in its last round (257 x 3 tiles over 256
+    workgroups) and mixes of long and short items; every head and row is
+    compared."""
     fa = _fa()
-    _say("bf16 causal many items", B, H, N)
+    _say("bf16 many items", B, H, N, "causal" if causal else "non-causal")
     shape = (B, H, N, 128)
     Q, K, V = (synth.torch_normal(700 + t, shape, "cuda", "bf16") for t in range(3))
     O = torch.full_like(Q, float("nan"))
     L = torch.full(shape[:3], float("nan"), device="cuda")
-    fa.fa_fwd(Q, K, V, O, L, causal=True)
+    fa.fa_fwd(Q, K, V, O, L, causal=causal)
     torch.cuda.synchronize()
     assert not torch.isnan(O).any() and not torch.isnan(L).any()
-    dO, dL = _prefill_compare(Q, K, V, O, L, 1 / math.sqrt(128), True)
+    dO, dL = _prefill_compare(Q, K, V, O, L, 1 / math.sqrt(128), causal)
     assert dO <= BF16_O and dL <= BF16_L, (dO, dL)
 
 
