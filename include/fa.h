@@ -60,8 +60,10 @@ typedef struct fa_fwd_plan_t {
   int q_tiles;               /* ceil(N / B_r) per (b, h) */
   int kv_tiles;              /* ceil(N / B_c) per (b, h) */
   int threads_per_workgroup; /* wavefronts * 64 */
-  int lds_bytes;             /* LDS per workgroup */
-  int64_t workgroups;        /* causal: min(work_units, compute units); else work_units */
+  int lds_bytes;             /* LDS per workgroup (d = 128 non-causal: with
+                                output staging rows) */
+  int64_t workgroups;        /* causal or d = 128: min(work_units, compute
+                                units); else work_units */
   int64_t tiles_visited;     /* (query tile, KV tile) pairs computed, all heads */
   int64_t tiles_masked;      /* of those, tiles masked on chip (diagonal/ragged) */
   int64_t work_units;        /* B * H * q_tiles, or B * H * ceil(q_tiles / 2)
@@ -225,8 +227,9 @@ int fa_decode_paged_splits(int B, int H, int max_blocks, int block_size, int num
 /* Host-only launch planning (no HIP call; usable without a GPU).
  * fa_fwd_plan: tile geometry and the exact number of tiles fa_fwd visits.
  * Causal fa_fwd runs a persistent grid of one workgroup per compute unit,
- * each taking every grid-th pair of query tiles; without a device the plan
- * assumes 256 compute units.  Non-causal fa_fwd runs one workgroup per
+ * each taking every grid-th pair of query tiles; so does non-causal fa_fwd
+ * at d = 128, with single query tiles.  Without a device the plan assumes
+ * 256 compute units.  Non-causal fa_fwd at d = 64 runs one workgroup per
  * query tile.
  * fa_decode_plan: splits and workspace; num_splits = 0 needs the device's CU
  * count, so without a device it assumes 256 compute units.
