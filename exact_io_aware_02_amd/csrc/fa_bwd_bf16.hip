@@ -77,13 +77,14 @@ __device__ __forceinline__ bf16x8_t to_bf16x8(const float* p) {
 
 // Copies `bytes` (a multiple of 1 KiB) of padded rows into LDS: every
 // wavefront of the workgroup issues its share of 1 KiB loads.  `voff_of`
-// gives the per-lane source offset of LDS byte o, within the tile whose
-// resource is `rsrc` (make_rsrc_from: rows past the head's end read zeros).
+// gives the per-lane source offset of LDS byte o within the tile, `soff` the
+// tile's offset in the head (the SGPR offset, which gfx950 includes in the
+// range check: rows past the head read zeros).
 template <typename F>
-__device__ __forceinline__ void dma_rows(const u32x4_t rsrc, char LDS_AS* dst, int bytes, int wave, int lane,
-                                         F voff_of) {
+__device__ __forceinline__ void dma_rows(const u32x4_t rsrc, unsigned soff, char LDS_AS* dst, int bytes, int wave,
+                                         int lane, F voff_of) {
   for (int blk = wave; blk < bytes / 1024; blk += kBwdWaves)
-    load_lds16(rsrc, (void LDS_AS*)(dst + blk * 1024), voff_of(blk * 1024 + lane * 16));
+    load_lds16_soff(rsrc, (void LDS_AS*)(dst + blk * 1024), voff_of(blk * 1024 + lane * 16), soff);
 }
 
 // Output rows of 32 x D in the accumulator layout (lane = row, registers =
@@ -178,18 +179,20 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ K
   // query tiles: causal items skip tiles whose every query precedes every key
   const int n_qt = (N + kBwdQT - 1) / kBwdQT;
   const int qt0 = CAUSAL ? (kt * kBwdKV) / kBwdQT : 0;
+  const u32x4_t q_rsrc = make_rsrc(Qg + head, head_bytes);
+  const u32x4_t do_rsrc = make_rsrc(dOg + head, head_bytes);
+  const u32x4_t l_rsrc = make_rsrc(Lg + (size_t)bh * N, (unsigned)N * 4);
+  const u32x4_t d_rsrc = make_rsrc(Dg + (size_t)bh * N, (unsigned)N * 4);
   auto issue = [&](int t, int s) {
     const unsigned soff = (unsigned)t * kBwdQT * T::kRowBytes;
-    dma_rows(make_rsrc_from(Qg + head, head_bytes, soff), qbuf(s), T::kQTBytes, wave, lane,
-             [](int o) { return padded_source<D>(o, true); });
-    dma_rows(make_rsrc_from(dOg + head, head_bytes, soff), dobuf(s), T::kQTBytes, wave, lane,
-             [](int o) { return padded_source<D>(o, true); });
+    dma_rows(q_rsrc, soff, qbuf(s), T::kQTBytes, wave, lane, [](int o) { return padded_source<D>(o, true); });
+    dma_rows(do_rsrc, soff, dobuf(s), T::kQTBytes, wave, lane, [](int o) { return padded_source<D>(o, true); });
     // 64 floats of L and D (lanes past them read zeros into the padding)
     if (wave == 0) {
       const unsigned so = (unsigned)t * kBwdQT * 4;
       const unsigned vo = lane < kBwdQT / 4 ? (unsigned)lane * 16 : 0x7FFFFFF0u;
-      load_lds16(make_rsrc_from(Lg + (size_t)bh * N, (unsigned)N * 4, so), (void LDS_AS*)lbuf(s), vo);
-      load_lds16(make_rsrc_from(Dg + (size_t)bh * N, (unsigned)N * 4, so), (void LDS_AS*)dbuf(s), vo);
+      load_lds16_soff(l_rsrc, (void LDS_AS*)lbuf(s), vo, so);
+      load_lds16_soff(d_rsrc, (void LDS_AS*)dbuf(s), vo, so);
     }
   };
 
@@ -341,12 +344,12 @@ void bwd_dq_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ Kg,
     const int last = min(N - 1, qt * kBwdQ + kBwdQ - 1);
     n_kt = min(n_kt, last / kBwdKT + 1);
   }
+  const u32x4_t k_rsrc = make_rsrc(Kg + head, head_bytes);
+  const u32x4_t v_rsrc = make_rsrc(Vg + head, head_bytes);
   auto issue = [&](int j, int s) {
     const unsigned soff = (unsigned)j * kBwdKT * T::kRowBytes;
-    dma_rows(make_rsrc_from(Kg + head, head_bytes, soff), kbuf(s), T::kKTBytes, wave, lane,
-             [](int o) { return padded_source<D>(o, true); });
-    dma_rows(make_rsrc_from(Vg + head, head_bytes, soff), vbuf(s), T::kKTBytes, wave, lane,
-             [](int o) { return padded_source<D>(o, true); });
+    dma_rows(k_rsrc, soff, kbuf(s), T::kKTBytes, wave, lane, [](int o) { return padded_source<D>(o, true); });
+    dma_rows(v_rsrc, soff, vbuf(s), T::kKTBytes, wave, lane, [](int o) { return padded_source<D>(o, true); });
   };
 
   const float c = scale * kLog2e;

@@ -149,3 +149,33 @@ def test_bwd_long_sequence_one_head():
         worst = _compare(Q, K, V, dO, dQ, dK, dV, causal, 1 / math.sqrt(128))
         print(f"N=16384 causal={causal} {worst}")
         assert max(worst.values()) <= 1.0, (causal, worst)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [100, 1000])
+def test_bwd_ragged_tail_reads_nothing_past_the_head(N, causal):
+    """Rows past N are not part of the problem: the backward's Q, dO, K, V
+    tiles and its L and D rows must read them as zeros, never as whatever
+    memory follows the last head.  Every input is a view at the start of an
+    allocation whose remainder holds NaN, so a read past the last head would
+    turn into NaN in a gradient; the reads stay inside the allocation either
+    way."""
+    fa = _fa()
+    _say("bwd ragged tail guard", N, causal)
+    shape = (1, 3, N, 128)
+    n = math.prod(shape)
+    views = []
+    for t in range(4):
+        buf = torch.full((n + 256 * 128,), float("nan"), device="cuda", dtype=torch.bfloat16)
+        buf[:n] = synth.torch_normal(830 + t, shape, "cuda", "bf16").reshape(-1)
+        views.append(buf[:n].view(shape))
+    Q, K, V, dO = views
+    obuf = torch.full((n + 256 * 128,), float("nan"), device="cuda", dtype=torch.bfloat16)
+    lbuf = torch.full((3 * N + 256,), float("nan"), device="cuda")
+    O, L = obuf[:n].view(shape), lbuf[:3 * N].view(shape[:3])
+    fa.fa_fwd(Q, K, V, O, L, causal=causal)
+    dQ, dK, dV = (torch.full_like(Q, float("nan")) for _ in range(3))
+    fa.fa_bwd(Q, K, V, O, dO, L, dQ, dK, dV, causal=causal)
+    torch.cuda.synchronize()
+    worst = _compare(Q, K, V, dO, dQ, dK, dV, causal, 1 / math.sqrt(128))
+    assert max(worst.values()) <= 1.0, worst
