@@ -84,7 +84,7 @@ template <typename F>
 __device__ __forceinline__ void dma_rows(const u32x4_t rsrc, unsigned soff, char LDS_AS* dst, int bytes, int wave,
                                          int lane, F voff_of) {
   for (int blk = wave; blk < bytes / 1024; blk += kBwdWaves)
-    load_lds16_soff(rsrc, (void LDS_AS*)(dst + blk * 1024), voff_of(blk * 1024 + lane * 16), soff);
+    load_lds16(rsrc, (void LDS_AS*)(dst + blk * 1024), voff_of(blk * 1024 + lane * 16), soff);
 }
 
 // Output rows of 32 x D in the accumulator layout (lane = row, registers =
@@ -191,8 +191,8 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ K
     if (wave == 0) {
       const unsigned so = (unsigned)t * kBwdQT * 4;
       const unsigned vo = lane < kBwdQT / 4 ? (unsigned)lane * 16 : 0x7FFFFFF0u;
-      load_lds16_soff(l_rsrc, (void LDS_AS*)lbuf(s), vo, so);
-      load_lds16_soff(d_rsrc, (void LDS_AS*)dbuf(s), vo, so);
+      load_lds16(l_rsrc, (void LDS_AS*)lbuf(s), vo, so);
+      load_lds16(d_rsrc, (void LDS_AS*)dbuf(s), vo, so);
     }
   };
 

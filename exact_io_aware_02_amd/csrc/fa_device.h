@@ -32,26 +32,16 @@ __host__ __device__ constexpr int vrow_perm(int k) {
 }
 
 // Buffer resource (4 descriptor words) over `bytes` bytes at `base`, no
-// stride.  A load whose VGPR + instruction offset is past the end returns
-// zeros and touches no memory.  Whether the load's SGPR offset counts in
-// that check differs between AMD GPU generations; gfx950 counts it (the
-// NaN-padded ragged-tail tests pin this).
+// stride.  A load whose offset is past the end returns zeros and touches no
+// memory.  Whether a load's SGPR offset counts in that check differs between
+// AMD GPU generations; gfx950 counts it, which the NaN-padded ragged-tail
+// tests pin, so the C++ kernels put a tile's offset there.  (The generated
+// d = 128 forward loop builds a resource per tile instead, at no cost.)
 __device__ __forceinline__ u32x4_t make_rsrc(const void* base, unsigned bytes) {
   const unsigned long long a = (unsigned long long)base;
   return u32x4_t{(unsigned)a, (unsigned)(a >> 32) & 0xFFFFu, bytes, 0x00020000u};
 }
-// Resource over bytes [off, bytes) of the buffer at `base` (empty when off
-// >= bytes): the loads of a tile that starts `off` bytes into a head, with
-// rows past the head's end reading zeros whatever the generation.  The
-// forward kernels load each tile through one.  The words are wavefront-
-// uniform; readfirstlane keeps them in SGPRs.
-__device__ __forceinline__ u32x4_t make_rsrc_from(const void* base, unsigned bytes, unsigned off) {
-  const u32x4_t r = make_rsrc((const char*)base + off, off < bytes ? bytes - off : 0u);
-  return u32x4_t{(unsigned)__builtin_amdgcn_readfirstlane((int)r[0]), (unsigned)__builtin_amdgcn_readfirstlane((int)r[1]),
-                 (unsigned)__builtin_amdgcn_readfirstlane((int)r[2]), r[3]};
-}
-// 16 bytes per lane from rsrc[voff] into LDS at lds + 16 * lane (voff past
-// the resource's end: zeros).
+// 16 bytes per lane from rsrc[voff + soff] into LDS at lds + 16 * lane.
 // Issued as asm so the compiler does not order it against LDS reads of other
 // buffers (it cannot prove them disjoint and would drain the queue); every
 // wait for these loads is explicit (vmcnt) in the kernels.  The compiler's
@@ -59,16 +49,7 @@ __device__ __forceinline__ u32x4_t make_rsrc_from(const void* base, unsigned byt
 // the wait states a buffer load needs after a VALU write of one of its SGPR
 // operands (v_readlane restoring a spilled descriptor: 5) and after the M0
 // write that sets the LDS address (1).
-__device__ __forceinline__ void load_lds16(u32x4_t rsrc, void LDS_AS* lds, unsigned voff) {
-  asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
-               :
-               : "v"(voff), "s"(rsrc), "{m0}"((unsigned)(size_t)lds)
-               : "memory");
-}
-// The same with a tile offset `soff` in the SGPR offset of the head's
-// resource (range-checked on gfx950, above).  The backward keeps this form:
-// per-tile resources cost its loops about 7 %.
-__device__ __forceinline__ void load_lds16_soff(u32x4_t rsrc, void LDS_AS* lds, unsigned voff, unsigned soff) {
+__device__ __forceinline__ void load_lds16(u32x4_t rsrc, void LDS_AS* lds, unsigned voff, unsigned soff) {
   asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
                :
                : "v"(voff), "s"(rsrc), "s"(soff), "{m0}"((unsigned)(size_t)lds)

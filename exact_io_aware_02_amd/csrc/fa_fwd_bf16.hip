@@ -142,14 +142,15 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ K
     v_voff[p] = padded_source<D>(o, true);
   }
   const unsigned head_bytes = (unsigned)N * D * 2;
-  // one K or V tile of the head at `head` (rows past N read as zeros)
-  auto dma_tile = [&](const __bf16* head, const unsigned* voff, int tile, char LDS_AS* dst) {
-    const u32x4_t rsrc = make_rsrc_from(head, head_bytes, (unsigned)tile * kFwdBC * T::kRowBytes);
+  // one K or V tile through the head's resource, the tile offset in the SGPR
+  // offset (range-checked on gfx950: rows past N read as zeros)
+  auto dma_tile = [&](const u32x4_t rsrc, const unsigned* voff, int tile, char LDS_AS* dst) {
+    const unsigned soff = (unsigned)tile * kFwdBC * T::kRowBytes;
 #pragma unroll
     for (int p = 0; p < T::kLoadsPerWave; ++p) {
       const int blk = wave + p * kFwdWaves;
       if (p + 1 < T::kLoadsPerWave || blk < T::kLoads)
-        load_lds16(rsrc, (void LDS_AS*)(dst + blk * 1024), voff[p]);
+        load_lds16(rsrc, (void LDS_AS*)(dst + blk * 1024), voff[p], soff);
     }
   };
 
@@ -200,9 +201,11 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ K
   };
   auto start_kv = [&](const int bh, const int qt) {
     const size_t head_off = (size_t)bh * N * D;
-    dma_tile(Kg + head_off, k_voff, 0, kbuf(0));
-    dma_tile(Vg + head_off, v_voff, 0, vbuf(0));
-    if (tiles_of(qt) > 1) dma_tile(Kg + head_off, k_voff, 1, kbuf(1));
+    const u32x4_t k_rsrc = make_rsrc(Kg + head_off, head_bytes);
+    const u32x4_t v_rsrc = make_rsrc(Vg + head_off, head_bytes);
+    dma_tile(k_rsrc, k_voff, 0, kbuf(0));
+    dma_tile(v_rsrc, v_voff, 0, vbuf(0));
+    if (tiles_of(qt) > 1) dma_tile(k_rsrc, k_voff, 1, kbuf(1));
   };
 
   // ---- one item: Algorithm 1 over its KV tiles, leaving (m, l, U).  Ends
@@ -212,8 +215,8 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ K
   const int qw0 = qt * kFwdBR + wave * 32;  // first query row of this wavefront
   const int qrow = qw0 + l32;               // the query this lane's column belongs to
   const int n_tiles = tiles_of(qt);
-  const __bf16* k_head = Kg + head_off;
-  const __bf16* v_head = Vg + head_off;
+  const u32x4_t k_rsrc = make_rsrc(Kg + head_off, head_bytes);
+  const u32x4_t v_rsrc = make_rsrc(Vg + head_off, head_bytes);
 
   // S^T tile (kFwdBC keys x 32 queries) from the K tile at `kb`: block c of
   // 32 keys accumulates in s[cb]
@@ -268,8 +271,8 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ K
   auto issue_slot = [&](int s) {
     if ((s & 1) == 0 && s >= 2) {
       const int t = s >> 1;
-      if (t + 1 < n_tiles) dma_tile(k_head, k_voff, t + 1, kbuf((t + 1) & 1));
-      if (t < n_tiles) dma_tile(v_head, v_voff, t, vbuf(t & 1));
+      if (t + 1 < n_tiles) dma_tile(k_rsrc, k_voff, t + 1, kbuf((t + 1) & 1));
+      if (t < n_tiles) dma_tile(v_rsrc, v_voff, t, vbuf(t & 1));
     }
   };
   auto end_slot = [&](int s) {
