@@ -50,6 +50,7 @@ through a VGPR: rows past N read as zeros and no load touches memory past
 the head, by construction.
 """
 
+import os
 import sys
 
 D = 128
@@ -78,6 +79,10 @@ V_MC2 = [ST + 14, ST + 15]   # m * c again, in VGPR banks 2, 3
 FRAG0 = 192                  # AGPR fragment slots a[192:255]
 NSLOT = 16
 LOOKAHEAD = 6
+# the buffer->LDS loads of a block are issued over its first LOAD_SPREAD of
+# MFMAs: they are waited for at the next step's top, and issued late they
+# leave too little time to cover the HBM latency
+LOAD_SPREAD = float(os.environ.get("FA_LOAD_SPREAD", "0.5"))
 
 # SGPRs used inside (declared as clobbers)
 S_J = 40        # tile index j
@@ -301,7 +306,7 @@ class Stream:
             for mf in mfs:
                 self.emit(mf(fi % NSLOT))
                 done += 1
-                while gi < len(groups) and done >= (gi + 1) * nmf // (len(groups) + 1):
+                while gi < len(groups) and done >= max(1, (gi + 1) * int(nmf * LOAD_SPREAD) // (len(groups) + 1)):
                     for ins in groups[gi]:
                         self.emit(ins)
                     gi += 1
