@@ -9,7 +9,10 @@ A step is one pass of the whole path over one batch of synthetic input:
      cache is not served from the 256 MB last-level cache.
 Inputs are resident in HBM before timing starts.  W untimed warm-up steps,
 then exactly K timed steps between device synchronisations; each kernel is
-bracketed by HIP events on the stream it is launched on.
+bracketed by HIP events on the stream it is launched on.  After an idle
+period the GPU's clock ramps up over its first few tens of launches (about
+35 ms of work: prefill_8k runs 1.15 ms per launch in the first ten, 0.87 ms
+from the fortieth on), so the default W = 60 steps times the steady state.
 
 Printed: one JSON line.  `value` is fa_fwd TFLOP/s on prefill_8k (algorithmic
 4*B*H*N^2*d FLOPs over the measured kernel time); decode GB/s (algorithmic
@@ -140,7 +143,8 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=60,
+                    help="untimed steps first (the clock ramps over the first ~40 launches after idle)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="host time budget of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip causal_4k and decode_varlen")
