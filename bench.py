@@ -267,7 +267,7 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
             "traffic": _traffic(None),
-            "kernel": "fwd_bf16_asm_kernel",
+            "kernel": "fwd_bf16_asm_kernel<false>",
             "ms_per_launch": round(fwd_ms, 5),
         },
         "decode": {

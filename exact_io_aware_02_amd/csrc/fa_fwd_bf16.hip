@@ -1,4 +1,5 @@
-// FlashAttention forward for bf16 Q/K/V on gfx950 (MI355X).
+// FlashAttention forward for bf16 Q/K/V on gfx950 (MI355X), head dimension
+// 64 (d = 128 runs fa_fwd_bf16_asm.hip, 64 rows per wavefront).
 //
 // What it computes is Algorithm 1 of "Infra: Flash Attention" (section
 // "Tiled computation and forward"), in the FlashAttention-2 order of the
@@ -516,8 +517,7 @@ hipError_t launch(const FwdArgs& a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, int d, hipStream_t stream) {
-  if (fwd_uses_asm(d, a.causal)) return launch_fwd_bf16_asm(a, stream);
-  if (d == 128) return launch<128, true>(a, stream);  // non-causal d = 128 runs the other kernel
+  if (fwd_uses_asm(d, a.causal)) return launch_fwd_bf16_asm(a, stream);  // d = 128
   return a.causal ? launch<64, true>(a, stream) : launch<64, false>(a, stream);
 }
 

@@ -1,4 +1,4 @@
-// FlashAttention forward for bf16 Q/K/V, d = 128, no causal mask, on gfx950:
+// FlashAttention forward for bf16 Q/K/V, d = 128, causal or not, on gfx950:
 // 64 query rows per wavefront, one wavefront per SIMD, the tile loop in
 // generated assembly.
 //
@@ -22,6 +22,9 @@
 //    and two probability tiles in VGPRs.  The compiler cannot hold that many
 //    values without spilling, so one query tile's loop is assembly generated
 //    by gen_fwd_asm.py with one fixed register for every value.
+//  * Causal: tiles wholly after a query tile are never visited; a
+//    wavefront masks its diagonal tile, and a tile wholly after its 64 rows
+//    (inside the query tile's range) gets zero weights through m c = +inf.
 //  * Persistent workgroups, one per compute unit: during an item's last
 //    product block the next item's Q fragments and first two K tiles load
 //    into the registers and K buffers that block no longer reads, and the
@@ -51,10 +54,11 @@ constexpr int kLds = kKV + kWaves * 64 * kStride;
 static_assert(kBR == kFwdBR && kBC == kFwdBC, "tiles must match the planner");
 static_assert(kKV == fwd_lds_bytes(D) && kLds == fwd_asm_lds_bytes(), "LDS size must match the planner");
 
+template <bool CAUSAL>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void fwd_bf16_asm_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ Kg,
                          const __bf16* __restrict__ Vg, __bf16* __restrict__ Og,
-                         float* __restrict__ Lg, int N, int q_tiles, int items, float scale) {
+                         float* __restrict__ Lg, int N, int q_tiles, int units, float scale) {
   __shared__ __attribute__((aligned(1024))) char smem[kLds];
   char LDS_AS* lds = (char LDS_AS*)smem;
   const unsigned lds_base = (unsigned)(size_t)lds;
@@ -87,35 +91,67 @@ void fwd_bf16_asm_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict
   const float c = scale * kLog2e;
   const float theta = 8.f / c;  // conditional-rescale threshold, raw score units
   const unsigned head_bytes = (unsigned)N * D * 2;
-  const int n = (N + kBC - 1) / kBC;
-  // keys past N are masked: the loop compares key - 4 g against N - 1 - 4 g
-  const int limg = N - 1 - 4 * g;
+  const int kv_tiles = (N + kBC - 1) / kBC;
+  // causal diagonal tile: key c + 4 g against query l32
+  const int dg = l32 - 4 * g;
 
-  // persistent: G workgroups take items lw, lw + G, ... (lw: the workgroup's
-  // logical index).  Dispatch is round-robin over the 8 XCDs and lw places a
-  // contiguous run of workgroups on one XCD, so the items running at once on
-  // an XCD are consecutive query tiles of the same heads and share K/V in
-  // that XCD's L2.
+  // persistent: G workgroups take units lw, lw + G, ... (lw: the workgroup's
+  // logical index).  A unit is a query tile, or for causal attention the
+  // pair of query tiles (p, q_tiles - 1 - p) of a head, the longer first, so
+  // that every causal unit has the same number of KV tiles.  Dispatch is
+  // round-robin over the 8 XCDs and lw places a contiguous run of workgroups
+  // on one XCD, so the units running at once on an XCD belong to the same
+  // heads and share K/V in that XCD's L2.
   const int G = gridDim.x;
   const int wg = blockIdx.x;
   const int per = G >> 3, rem = G & 7;
   const int xcd = wg & 7, slot_id = wg >> 3;
   const int lw = xcd * per + (xcd < rem ? xcd : rem) + slot_id;
+  const int pairs = (q_tiles + 1) >> 1;
+  auto item_of = [&](int unit, int second, int& bh, int& qt) {
+    if (CAUSAL) {
+      bh = unit / pairs;
+      const int p = unit - bh * pairs;
+      qt = second ? p : q_tiles - 1 - p;
+    } else {
+      bh = unit / q_tiles;
+      qt = unit - bh * q_tiles;
+    }
+  };
+  // the item after (unit, second) in this workgroup's sequence
+  auto advance = [&](int& unit, int& second) {
+    if (CAUSAL && second == 0) {
+      const int p = unit - (unit / pairs) * pairs;
+      if (p < q_tiles - 1 - p) {
+        second = 1;
+        return;
+      }
+    }
+    second = 0;
+    unit += G;
+  };
 
-  int it = lw;
+  int unit = lw, second = 0;
   int pre = 0;
-  while (it < items) {
-    const int bh = it / q_tiles;
-    const int qt = it - bh * q_tiles;
-    const int nit = it + G;
-    const bool more = nit < items;
-    const int nbh = more ? nit / q_tiles : bh;
-    const int nqt = more ? nit - nbh * q_tiles : qt;
+  while (unit < units) {
+    int bh, qt;
+    item_of(unit, second, bh, qt);
+    int nunit = unit, nsecond = second;
+    advance(nunit, nsecond);
+    const bool more = nunit < units;
+    int nbh = bh, nqt = qt;
+    if (more) item_of(nunit, nsecond, nbh, nqt);
 
     const size_t head_off = (size_t)bh * N * D;
     const size_t nhead_off = (size_t)nbh * N * D;
     const int qw0 = __builtin_amdgcn_readfirstlane(qt * kBR + wave * 64);
     const int nqw0 = nqt * kBR + wave * 64;
+    // KV tiles of the item (causal: those wholly after its last row skipped)
+    const int n = CAUSAL ? min(kv_tiles, min(N - 1, qt * kBR + kBR - 1) / kBC + 1) : kv_tiles;
+    // keys past the lane's last valid one (N - 1, or causal its query) are
+    // masked: the loop compares key - 4 g against the limit - 4 g
+    const int limg0 = (CAUSAL ? min(N - 1, qw0 + l32) : N - 1) - 4 * g;
+    const int limg1 = (CAUSAL ? min(N - 1, qw0 + 32 + l32) : N - 1) - 4 * g;
     const u32x4_t q_rsrc = make_rsrc(Qg + head_off, head_bytes);
     const u32x4_t nq_rsrc = make_rsrc(Qg + nhead_off, more ? head_bytes : 0u);
     const u32x4_t o_rsrc = make_rsrc(Og + head_off, head_bytes);
@@ -132,38 +168,46 @@ void fwd_bf16_asm_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict
     const unsigned nqvo = (unsigned)(nqw0 + l32) * D * 2 + g * 16;
     const unsigned ovo = (unsigned)(qw0 + (lane >> 4)) * D * 2 + (lane & 15) * 16;
     const unsigned lvo = (unsigned)(qw0 + l32) * 4;
-    asm volatile(FA_ASM_ITEM
-                 :
-                 : [kvo0] "v"(kvo[0]), [kvo1] "v"(kvo[1]), [kvo2] "v"(kvo[2]), [kvo3] "v"(kvo[3]),
-                   [kvo4] "v"(kvo[4]), [vvo0] "v"(vvo[0]), [vvo1] "v"(vvo[1]), [vvo2] "v"(vvo[2]),
-                   [vvo3] "v"(vvo[3]), [vvo4] "v"(vvo[4]), [qvo] "v"(qvo), [nqvo] "v"(nqvo), [kb] "v"(kb),
-                   [vb] "v"(vb), [stg] "v"(stg), [srd] "v"(srd), [ovo] "v"(ovo), [lvo] "v"(lvo),
-                   [limg0] "v"(limg), [limg1] "v"(limg), [c] "v"(c), [theta] "v"(theta),
-                   [qrsrc] "s"(q_rsrc), [nqrsrc] "s"(nq_rsrc), [orsrc] "s"(o_rsrc), [lrsrc] "s"(l_rsrc),
-                   [klo] "s"(klo), [khi] "s"(khi), [vlo] "s"(vlo), [vhi] "s"(vhi), [hb] "s"(head_bytes),
-                   [nklo] "s"(nklo), [nkhi] "s"(nkhi), [nhb] "s"(nhb), [n] "s"(n), [wave] "s"(wave),
-                   [wbase] "s"(wbase), [n_keys] "s"(N), [qw0] "s"(qw0), [pre] "s"(pre)
-                 : FA_ASM_CLOBBERS);
+#define FA_ASM_OPERANDS                                                                                          \
+  :                                                                                                              \
+  : [kvo0] "v"(kvo[0]), [kvo1] "v"(kvo[1]), [kvo2] "v"(kvo[2]), [kvo3] "v"(kvo[3]), [kvo4] "v"(kvo[4]),           \
+    [vvo0] "v"(vvo[0]), [vvo1] "v"(vvo[1]), [vvo2] "v"(vvo[2]), [vvo3] "v"(vvo[3]), [vvo4] "v"(vvo[4]),           \
+    [qvo] "v"(qvo), [nqvo] "v"(nqvo), [kb] "v"(kb), [vb] "v"(vb), [stg] "v"(stg), [srd] "v"(srd), [ovo] "v"(ovo), \
+    [lvo] "v"(lvo), [limg0] "v"(limg0), [limg1] "v"(limg1), [dg] "v"(dg), [c] "v"(c), [theta] "v"(theta),        \
+    [qrsrc] "s"(q_rsrc), [nqrsrc] "s"(nq_rsrc), [orsrc] "s"(o_rsrc), [lrsrc] "s"(l_rsrc), [klo] "s"(klo),        \
+    [khi] "s"(khi), [vlo] "s"(vlo), [vhi] "s"(vhi), [hb] "s"(head_bytes), [nklo] "s"(nklo), [nkhi] "s"(nkhi),    \
+    [nhb] "s"(nhb), [n] "s"(n), [wave] "s"(wave), [wbase] "s"(wbase), [n_keys] "s"(N), [qw0] "s"(qw0),           \
+    [pre] "s"(pre)                                                                                               \
+  : FA_ASM_CLOBBERS
+    if constexpr (CAUSAL)
+      asm volatile(FA_ASM_ITEM_CAUSAL FA_ASM_OPERANDS);
+    else
+      asm volatile(FA_ASM_ITEM FA_ASM_OPERANDS);
+#undef FA_ASM_OPERANDS
     pre = 1;
-    it = nit;
+    unit = nunit;
+    second = nsecond;
   }
   // the last item's stores (and its empty prefetch) complete before the
   // workgroup's LDS and registers are released
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
+template <bool CAUSAL>
 hipError_t launch(const FwdArgs& a, hipStream_t stream) {
   const int q_tiles = (a.N + kBR - 1) / kBR;
-  const int64_t items = (int64_t)a.B * a.H * q_tiles;
-  hipLaunchKernelGGL(fwd_bf16_asm_kernel, dim3((unsigned)a.grid), dim3(kThreads), 0, stream,
+  const int64_t units = fwd_units(a.B, a.H, a.N, a.causal);
+  hipLaunchKernelGGL((fwd_bf16_asm_kernel<CAUSAL>), dim3((unsigned)a.grid), dim3(kThreads), 0, stream,
                      static_cast<const __bf16*>(a.Q), static_cast<const __bf16*>(a.K),
                      static_cast<const __bf16*>(a.V), static_cast<__bf16*>(a.O), a.L, a.N, q_tiles,
-                     (int)items, a.scale);
+                     (int)units, a.scale);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_fwd_bf16_asm(const FwdArgs& a, hipStream_t stream) { return launch(a, stream); }
+hipError_t launch_fwd_bf16_asm(const FwdArgs& a, hipStream_t stream) {
+  return a.causal ? launch<true>(a, stream) : launch<false>(a, stream);
+}
 
 }  // namespace fa

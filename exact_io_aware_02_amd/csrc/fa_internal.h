@@ -99,11 +99,10 @@ struct DecodeArgs {
   int max_blocks = 0, log2_bs = 0, num_blocks = 0;
 };
 
-// bf16 prefill with d = 128 and no causal mask runs the 64-rows-per-wavefront
-// kernel (4 wavefronts of 64 query rows, tile loop in generated assembly);
-// every other bf16 prefill the 32-rows-per-wavefront one (8 wavefronts).
-// Both use the tiles above.
-inline bool fwd_uses_asm(int d, int causal) { return d == 128 && !causal; }
+// bf16 prefill with d = 128 runs the 64-rows-per-wavefront kernel (4
+// wavefronts of 64 query rows, tile loop in generated assembly); d = 64 the
+// 32-rows-per-wavefront one (8 wavefronts).  Both use the tiles above.
+inline bool fwd_uses_asm(int d, int causal) { (void)causal; return d == 128; }
 inline int fwd_lds_for(int d, int causal) { return fwd_uses_asm(d, causal) ? fwd_asm_lds_bytes() : fwd_lds_bytes(d); }
 inline int fwd_threads(int d, int causal) { return fwd_uses_asm(d, causal) ? 4 * 64 : kFwdWaves * 64; }
 

@@ -4,10 +4,11 @@ FlashAttention forward (64 query rows per wavefront, one wavefront per SIMD).
     python exact_io_aware_02_amd/gen_fwd_asm.py OUT.inc
 
 The build runs this before compiling fa_fwd_bf16_asm.hip, which includes the
-output: the C string macro FA_ASM_ITEM, the body of one inline-asm statement
-that runs Algorithm 1 of "Infra: Flash Attention" ("Tiled computation and
-forward") without a causal mask for one query tile of a wavefront and stores
-its rows of O = U / l (bf16) and L = m + log l (keys past N are masked).
+output: the C string macros FA_ASM_ITEM and FA_ASM_ITEM_CAUSAL, the bodies of
+inline-asm statements that run Algorithm 1 of "Infra: Flash Attention"
+("Tiled computation and forward"), without and with the causal mask, for one
+query tile of a wavefront and store its rows of O = U / l (bf16) and
+L = m + log l (keys past N are masked).
 While its last product block runs, an item loads the next item's Q, K_0 and
 K_1, so a persistent workgroup's items follow one another with no wait for
 those loads.
@@ -392,46 +393,82 @@ def dma_tile(st, kind, dst_off, tile_sgpr, label):
     st.emit(f"{label}_%=:")
 
 
+def cmp_mask(st, elems):
+    """elems: (score register, threshold register, c): the score becomes -inf
+    where c > threshold.  Three compare masks rotate, so that every mask is
+    read three instructions after it is written."""
+    pend = []
+    for k, (reg, thr, c) in enumerate(elems):
+        sp = S_CMP[k % 3]
+        st.emit(f"v_cmp_lt_i32_e64 s[{sp}:{sp + 1}], v{thr}, {c}")
+        pend.append((reg, sp))
+        if len(pend) == 3:
+            for r, m in pend:
+                st.emit(f"v_cndmask_b32_e64 v{r}, v{r}, v{V_NINF}, s[{m}:{m + 1}]")
+            pend = []
+    for r, m in pend:
+        st.emit("s_nop 1")
+        st.emit(f"v_cndmask_b32_e64 v{r}, v{r}, v{V_NINF}, s[{m}:{m + 1}]")
+
+
 def mask_block(st, sbuf, causal, label):
-    """Scores of the tile at key base 64 j (in s[S_J]) set to -inf where the
-    key is past the last valid one of the lane's query: key kbase + c + 4 g
-    against lim (thresholds in %[limg0/1] = lim - 4 g)."""
+    """Masking of the score tile at key base 64 j (j in s[S_J]) before its
+    softmax.  Lane (l32, g) holds, for query block qb, the keys kbase + c + 4 g
+    with c = 32 cb + 8 (i >> 2) + (i & 3) for element i of s[cb][qb].
+      * a tile reaching past N: every key past the lane's last valid one
+        (thresholds %[limg0/1] = lim - 4 g, lim = N - 1 or, causal,
+        min(N - 1, query)) is set to -inf;
+    causal only (the wavefront's rows are qw0 .. qw0 + 63):
+      * the diagonal tile (kbase = qw0): key c + 4 g of query block qb is
+        masked against query 32 qb + l32, i.e. the lower-left 32 x 32 block is
+        kept, the upper-right one dropped, and the two diagonal blocks compare
+        c against %[dg] = l32 - 4 g;
+      * a tile wholly after the rows (kbase > qw0): every weight is zero, which
+        m c = +inf gives for the whole tile (restored after the step)."""
     st.emit(f"s_lshl_b32 s{S_KB}, s{S_J}, 6")
-    # skip unless the tile reaches past a row's limit: causal kbase + 63 > qw0,
-    # or kbase + 64 > N
     st.emit(f"s_add_u32 s{S_T1}, s{S_KB}, 64")
     st.emit(f"s_cmp_gt_u32 s{S_T1}, %[n_keys]")
-    st.emit(f"s_cbranch_scc1 {label}_do_%=")
+    st.emit(f"s_cbranch_scc1 {label}_gen_%=")
     if causal:
-        st.emit(f"s_add_u32 s{S_T1}, s{S_KB}, 63")
-        st.emit(f"s_cmp_gt_u32 s{S_T1}, %[qw0]")
-        st.emit(f"s_cbranch_scc1 {label}_do_%=")
+        st.emit(f"s_cmp_eq_u32 s{S_KB}, %[qw0]")
+        st.emit(f"s_cbranch_scc1 {label}_diag_%=")
+        st.emit(f"s_cmp_gt_u32 s{S_KB}, %[qw0]")
+        st.emit(f"s_cbranch_scc1 {label}_full_%=")
     st.emit(f"s_branch {label}_end_%=")
-    st.emit(f"{label}_do_%=:")
+    sb = S_BUF[sbuf]
+    # general: thresholds against the tile's key base (the scores were
+    # written by MFMAs a step ago; the nops cover the rest of their latency
+    # for a tile read right after its product)
+    st.emit(f"{label}_gen_%=:")
     st.emit("s_nop 15")
     st.emit("s_nop 15")
     st.emit("s_nop 15")
     for qb in range(2):
         st.emit(f"v_subrev_u32 v{V_THR[qb]}, s{S_KB}, %[limg{qb}]")
-    k = 0
-    pend = []
-    sb = S_BUF[sbuf]
+    elems = []
     for qb in range(2):
         for cb in range(2):
             for i in range(16):
-                c = 32 * cb + 8 * (i >> 2) + (i & 3)
-                reg = sb + (2 * cb + qb) * 16 + i
-                sp = S_CMP[k % 3]
-                st.emit(f"v_cmp_lt_i32_e64 s[{sp}:{sp + 1}], v{V_THR[qb]}, {c}")
-                pend.append((reg, sp))
-                k += 1
-                if len(pend) == 3:
-                    for r, s in pend:
-                        st.emit(f"v_cndmask_b32_e64 v{r}, v{r}, v{V_NINF}, s[{s}:{s + 1}]")
-                    pend = []
-    for r, s in pend:
-        st.emit("s_nop 1")
-        st.emit(f"v_cndmask_b32_e64 v{r}, v{r}, v{V_NINF}, s[{s}:{s + 1}]")
+                elems.append((sb + (2 * cb + qb) * 16 + i, V_THR[qb], 32 * cb + 8 * (i >> 2) + (i & 3)))
+    cmp_mask(st, elems)
+    if causal:
+        st.emit(f"s_branch {label}_end_%=")
+        st.emit(f"{label}_diag_%=:")
+        st.emit("s_nop 15")
+        st.emit("s_nop 15")
+        st.emit("s_nop 15")
+        for i in range(16):
+            st.emit(f"v_mov_b32 v{sb + (2 * 1 + 0) * 16 + i}, v{V_NINF}")
+        st.emit(f"v_mov_b32 v{V_THR[0]}, %[dg]")
+        elems = []
+        for cb, qb in ((0, 0), (1, 1)):
+            for i in range(16):
+                elems.append((sb + (2 * cb + qb) * 16 + i, V_THR[0], 8 * (i >> 2) + (i & 3)))
+        cmp_mask(st, elems)
+        st.emit(f"s_branch {label}_end_%=")
+        st.emit(f"{label}_full_%=:")
+        for r in V_MC + V_MC2:
+            st.emit(f"v_mov_b32 v{r}, 0x7f800000")
     st.emit(f"{label}_end_%=:")
 
 
@@ -483,6 +520,12 @@ def step(st, parity, causal, kind, label):
     else:
         frags = qk_frags(1, 1)
     st.block(frags, valu, valu_first=(40 if kind == "first" else 8), groups=groups)
+    if causal:
+        # m c again (a tile after the rows set it to +inf)
+        for qb in range(2):
+            st.emit(f"v_mul_f32 v{V_MC[qb]}, s{S_C}, v{V_M[qb]}")
+        for qb in range(2):
+            st.emit(f"v_mov_b32 v{V_MC2[qb]}, v{V_MC[qb]}")
     if kind != "first":
         # conditional rescaling ("Invariant of conditional rescaling"): the
         # base moves only if a weight relative to it exceeds 2^8, which only
@@ -695,7 +738,7 @@ def clobbers():
 def main(out):
     with open(out, "w") as f:
         f.write("// Generated by gen_fwd_asm.py; do not edit.\n#pragma once\n\n")
-        for name, causal in (("FA_ASM_ITEM", False),):
+        for name, causal in (("FA_ASM_ITEM", False), ("FA_ASM_ITEM_CAUSAL", True)):
             body = item_asm(causal)
             f.write(f"#define {name} \\\n")
             for ins in body:

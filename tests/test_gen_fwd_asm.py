@@ -1,5 +1,5 @@
-"""Checks, on the CPU, the generated assembly of the 64-rows-per-wavefront
-forward's tile loop (exact_io_aware_02_amd/gen_fwd_asm.py) against the
+"""Checks, on the CPU, the generated assembly (without and with the causal
+mask) of the 64-rows-per-wavefront forward's tile loop (exact_io_aware_02_amd/gen_fwd_asm.py) against the
 rules the generator states for the hazards it handles itself:
 
   * every LDS read has landed (s_waitcnt lgkmcnt) before an MFMA or VALU
@@ -79,10 +79,10 @@ def _wait_states(op, line):
     return 1
 
 
-@pytest.fixture(scope="module")
-def program():
+@pytest.fixture(scope="module", params=[False, True], ids=["non-causal", "causal"])
+def program(request):
     g = _gen()
-    return g, [ln for ln in g.item_asm(False)]
+    return g, [ln for ln in g.item_asm(request.param)]
 
 
 def test_register_homes_are_disjoint(program):
