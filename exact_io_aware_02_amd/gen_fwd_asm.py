@@ -51,7 +51,6 @@ through a VGPR: rows past N read as zeros and no load touches memory past
 the head, by construction.
 """
 
-import os
 import sys
 
 D = 128
@@ -83,7 +82,8 @@ LOOKAHEAD = 6
 # the buffer->LDS loads of a block are issued over its first LOAD_SPREAD of
 # MFMAs: they are waited for at the next step's top, and issued late they
 # leave too little time to cover the HBM latency
-LOAD_SPREAD = float(os.environ.get("FA_LOAD_SPREAD", "0.5"))
+LOAD_SPREAD = 0.5
+VALU_LEAD = 8                # softmax instructions issued before a step's first MFMA
 
 # SGPRs used inside (declared as clobbers)
 S_J = 40        # tile index j
@@ -519,7 +519,7 @@ def step(st, parity, causal, kind, label):
         frags = pv_frags(1 - j_odd, 1 - j_odd)
     else:
         frags = qk_frags(1, 1)
-    st.block(frags, valu, valu_first=(40 if kind == "first" else 8), groups=groups)
+    st.block(frags, valu, valu_first=(40 if kind == "first" else VALU_LEAD), groups=groups)
     if causal:
         # m c again (a tile after the rows set it to +inf)
         for qb in range(2):
