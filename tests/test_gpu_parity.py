@@ -232,17 +232,22 @@ def test_bf16_base_moves_in_later_tiles(N):
         assert dO <= BF16_O and dL <= BF16_L, (causal, dO, dL)
 
 
-def test_bf16_L_optional_and_deterministic():
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bf16_L_optional_and_deterministic(causal, d):
+    """O does not depend on whether L is requested (L = NULL: the kernels'
+    L stores go nowhere), and repeated launches give the same bits."""
     fa = _fa()
-    _say("bf16 determinism")
-    shape = (1, 4, 1000, 128)
+    _say("bf16 determinism", causal, d)
+    shape = (1, 4, 1000, d)
     Q, K, V = (synth.torch_normal(400 + t, shape, "cuda", "bf16") for t in range(3))
-    O1, O2 = torch.empty_like(Q), torch.empty_like(Q)
-    L1 = torch.empty(shape[:3], device="cuda")
-    fa.fa_fwd(Q, K, V, O1, L1, causal=True)
-    fa.fa_fwd(Q, K, V, O2, None, causal=True)
+    O1, O2, O3 = torch.empty_like(Q), torch.empty_like(Q), torch.empty_like(Q)
+    L1, L3 = torch.empty(shape[:3], device="cuda"), torch.empty(shape[:3], device="cuda")
+    fa.fa_fwd(Q, K, V, O1, L1, causal=causal)
+    fa.fa_fwd(Q, K, V, O2, None, causal=causal)
+    fa.fa_fwd(Q, K, V, O3, L3, causal=causal)
     torch.cuda.synchronize()
-    assert torch.equal(O1, O2)
+    assert torch.equal(O1, O2) and torch.equal(O1, O3) and torch.equal(L1, L3)
 
 
 def _rows_sample(N, seed):
