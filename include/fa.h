@@ -60,8 +60,8 @@ typedef struct fa_fwd_plan_t {
   int q_tiles;               /* ceil(N / B_r) per (b, h) */
   int kv_tiles;              /* ceil(N / B_c) per (b, h) */
   int threads_per_workgroup; /* wavefronts * 64 */
-  int lds_bytes;             /* LDS per workgroup (d = 128 non-causal: with
-                                output staging rows) */
+  int lds_bytes;             /* LDS per workgroup (d = 128: with output
+                                staging rows) */
   int64_t workgroups;        /* causal or d = 128: min(work_units, compute
                                 units); else work_units */
   int64_t tiles_visited;     /* (query tile, KV tile) pairs computed, all heads */
