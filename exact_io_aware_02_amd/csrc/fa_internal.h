@@ -12,10 +12,11 @@ namespace fa {
 // KV tiles of kFwdBC keys.
 constexpr int kFwdWaves = 8;
 constexpr int kFwdBR = 32 * kFwdWaves;
-#ifndef FA_FWD_BC
-#define FA_FWD_BC 64
-#endif
-constexpr int kFwdBC = FA_FWD_BC;
+// B_c is fixed at 64.  The buffer->LDS load helper pads its asm with
+// wait states for the SGPR operands it reads (fa_device.h, load_lds16); that
+// padding has been exercised with these tiles only, so no other B_c is
+// built.
+constexpr int kFwdBC = 64;
 // LDS of one prefill workgroup: two K and two V tiles, each row padded by 16
 // bytes (the query tile lives in registers).
 __host__ __device__ constexpr int fwd_lds_bytes(int d) { return 4 * kFwdBC * (2 * d + 16); }

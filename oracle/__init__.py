@@ -25,7 +25,9 @@ Sources (three web pages on one subject; cited by title and section):
 Modules:
 
 * ``attention``  -- the plain definition: O = softmax(Q K^T * scale) V and
-  L = log-sum-exp per row, causal or not, plus the single-query decode form.
+  L = log-sum-exp per row, causal or not, plus the single-query decode form,
+  and the P-weighted spread of V around O (a bound on the effect of rounding
+  P before the product with V).
 * ``online``     -- scalar online softmax, the (m, l, u) block state and its
   merge, and the Flash-Decoding combine of (O^(k), m^(k), l^(k)) partials.
 * ``tiled``      -- Algorithm 1 of "Infra: Flash Attention" taken step by step
@@ -42,7 +44,7 @@ Parity status: every function here is pinned by a CPU test under ``tests/``
 None is "parity unpinned".
 """
 
-from .attention import attention_ref, attention_rows, decode_ref
+from .attention import attention_ref, attention_rows, attention_dev_rows, decode_ref
 from .online import (
     online_softmax,
     block_state,
@@ -58,6 +60,7 @@ from .backward import attention_backward, attention_backward_ref, attention_back
 __all__ = [
     "attention_ref",
     "attention_rows",
+    "attention_dev_rows",
     "decode_ref",
     "online_softmax",
     "block_state",

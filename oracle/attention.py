@@ -14,6 +14,9 @@ scope"; the per-row log-sum-exp from section "Backward and recomputation"):
     O_i = sum_j exp(S_ij - m_i) V_j / l_i
     L_i = m_i + log(l_i)  = log sum_j exp(S_ij)   (natural logarithm)
 
+attention_dev_rows gives, from the same definition, the P-weighted spread of
+V around O that bounds the effect of rounding P before the product with V.
+
 This is the definition, not the tiled algorithm: the whole row of scores is
 formed (a block of rows at a time only to bound memory) and reduced with
 numpy.  Inputs are upcast to float64 exactly (bf16 and fp32 values are exactly
@@ -90,6 +93,46 @@ def attention_ref(Q, K, V, scale, causal=False):
     for s in range(Qf.shape[0]):
         O[s], L[s] = attention_rows(Qf[s], Kf[s], Vf[s], scale, causal)
     return O.reshape(lead + (N, Vf.shape[-1])), L.reshape(lead + (N,))
+
+
+def attention_dev_rows(q, k, v, scale, causal=False, q_pos=None):
+    """Per selected row i and value dimension e, with P the exact attention
+    probabilities of the definition and O = P V:
+
+        dev[i, e]    = sum_j P_ij |V_je - O_ie|   (P-weighted mean absolute
+                                                   deviation of V around O)
+        absmean[i, e] = sum_j P_ij |V_je|
+
+    These bound how far O moves when every probability is perturbed by a
+    relative amount of at most delta and the result is renormalised by the
+    perturbed weights: |O' - O| <= delta / (1 - delta) * dev.  That is the
+    effect of rounding the probabilities to a narrower format before the
+    product with V (the probability matrix W of "Infra: Flash Attention",
+    Algorithm 1, entering U = alpha U + W V).  Arguments as attention_rows.
+    Returns float64 (dev [R, dv], absmean [R, dv]).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    if q_pos is None:
+        q_pos = np.arange(q.shape[0])
+    q_pos = np.asarray(q_pos, dtype=np.int64)
+    o, lse = attention_rows(q, k, v, scale, causal=causal, q_pos=q_pos)
+    R, dv = o.shape
+    dev = np.zeros((R, dv), dtype=np.float64)
+    absmean = np.zeros((R, dv), dtype=np.float64)
+    rb = max(1, (1 << 20) // max(1, k.shape[0] * dv // 64))
+    for r0 in range(0, R, rb):
+        r1 = min(R, r0 + rb)
+        s = (q[r0:r1] @ k.T) * float(scale)
+        if causal:
+            s = np.where(np.arange(k.shape[0])[None, :] <= q_pos[r0:r1, None], s, -np.inf)
+        ok = np.isfinite(lse[r0:r1])
+        p = np.where(ok[:, None], np.exp(s - np.where(ok, lse[r0:r1], 0.0)[:, None]), 0.0)
+        for e in range(dv):
+            dev[r0:r1, e] = np.sum(p * np.abs(v[None, :, e] - o[r0:r1, e, None]), axis=1)
+        absmean[r0:r1] = p @ np.abs(v)
+    return dev, absmean
 
 
 def decode_ref(q, K, V, scale):

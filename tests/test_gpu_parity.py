@@ -1,11 +1,11 @@
 """Parity of the HIP path (through the C ABI) with the float64 oracle.
 
-Bars: bf16 inputs -- max|dO| <= 2e-2 and max|dL| <= 2e-3; fp32 inputs --
-max|dO| <= 1e-5 and max|dL| <= 1e-5 (absolute, max over the elements
-compared).  Small shapes are compared element by element; the full-size
-workloads are run in the same launch configuration the bench times and
-compared on sampled rows that the oracle computes one by one (every row of a
-decode workload is one such sample).
+Bars (tests/parity_util.py): bf16 inputs -- |dO| <= 2e-2 (one bf16 spacing
+where |O| >= 8, since the bf16 output alone may then be more than 2e-2 away)
+and |dL| <= 2e-3; fp32 inputs -- |dO| <= 1e-5 and |dL| <= 1e-5 (absolute,
+per element).  Small shapes and the five workloads are compared element by
+element, the workloads in the launch configuration the bench times; only the
+inputs larger than the workloads are compared on sampled rows.
 """
 
 import math
@@ -19,8 +19,7 @@ import synth
 
 pytestmark = pytest.mark.gpu
 
-BF16_O, BF16_L = 2e-2, 2e-3
-F32_O, F32_L = 1e-5, 1e-5
+from tests.parity_util import BF16_L, BF16_O, Cmp, rounded_w_bound
 
 
 def _fa():
@@ -41,20 +40,19 @@ def _host(t):
 
 def _prefill_compare(Q, K, V, O, L, scale, causal, rows=None, heads=None):
     """Compare device outputs with the oracle on the given (b, h) heads and
-    query rows (all when None).  Returns (max|dO|, max|dL|)."""
+    query rows (all when None).  Returns a Cmp (bf16 bars unless Q is fp32)."""
     B, H, N, d = Q.shape
     heads = heads if heads is not None else [(b, h) for b in range(B) for h in range(H)]
-    dO = dL = 0.0
+    c = Cmp(bf16=Q.dtype != torch.float32)
+    r = np.arange(N) if rows is None else np.asarray(rows)
+    ri = None if rows is None else torch.as_tensor(r, device=Q.device)
     for b, h in heads:
-        r = np.arange(N) if rows is None else np.asarray(rows)
-        q = _host(Q[b, h, torch.as_tensor(r, device=Q.device)])
+        pick = (lambda t: t[b, h]) if ri is None else (lambda t: t[b, h, ri])
         k, v = _host(K[b, h]), _host(V[b, h])
-        o_ref, l_ref = oracle.attention_rows(q, k, v, scale, causal=causal, q_pos=r)
-        o_dev = _host(O[b, h, torch.as_tensor(r, device=O.device)])
-        l_dev = _host(L[b, h, torch.as_tensor(r, device=L.device)])
-        dO = max(dO, float(np.max(np.abs(o_dev - o_ref))))
-        dL = max(dL, float(np.max(np.abs(l_dev - l_ref))))
-    return dO, dL
+        o_ref, l_ref = oracle.attention_rows(_host(pick(Q)), k, v, scale, causal=causal, q_pos=r)
+        c.add_o(_host(pick(O)), o_ref)
+        c.add_l(_host(pick(L)), l_ref)
+    return c
 
 
 # --------------------------------------------------------------------------
@@ -71,9 +69,9 @@ def test_fp32_small_workload_all_elements():
     scale = 1.0 / math.sqrt(cfg["d"])
     fa.fa_fwd_f32(Q, K, V, O, L, causal=False, scale=scale)
     torch.cuda.synchronize()
-    dO, dL = _prefill_compare(Q, K, V, O, L, scale, False)
-    print(f"fp32_small max|dO|={dO:.3e} max|dL|={dL:.3e}")
-    assert dO <= F32_O and dL <= F32_L
+    c = _prefill_compare(Q, K, V, O, L, scale, False)
+    print("fp32_small", c)
+    assert c.ok(), c
 
 
 def test_fp32_worked_example_49_over_15():
@@ -109,8 +107,8 @@ def test_fp32_small_shapes(N, d, causal):
     L = torch.empty(shape[:3], device="cuda")
     fa.fa_fwd_f32(Q, K, V, O, L, causal=causal)
     torch.cuda.synchronize()
-    dO, dL = _prefill_compare(Q, K, V, O, L, 1 / math.sqrt(d), causal)
-    assert dO <= F32_O and dL <= F32_L, (dO, dL)
+    c = _prefill_compare(Q, K, V, O, L, 1 / math.sqrt(d), causal)
+    assert c.ok(), c
 
 
 # --------------------------------------------------------------------------
@@ -129,8 +127,8 @@ def test_bf16_small_shapes(N, d, causal):
     L = torch.empty(shape[:3], device="cuda")
     fa.fa_fwd(Q, K, V, O, L, causal=causal)
     torch.cuda.synchronize()
-    dO, dL = _prefill_compare(Q, K, V, O, L, 1 / math.sqrt(d), causal)
-    assert dO <= BF16_O and dL <= BF16_L, (dO, dL)
+    c = _prefill_compare(Q, K, V, O, L, 1 / math.sqrt(d), causal)
+    assert c.ok(), c
 
 
 @pytest.mark.parametrize("d", [64, 128])
@@ -157,8 +155,8 @@ def test_bf16_ragged_tail_reads_nothing_past_the_head(N, d):
         fa.fa_fwd(Q, K, V, O, L, causal=causal)
         torch.cuda.synchronize()
         assert not torch.isnan(O).any() and not torch.isnan(L).any(), causal
-        dO, dL = _prefill_compare(Q, K, V, O, L, 1 / math.sqrt(d), causal)
-        assert dO <= BF16_O and dL <= BF16_L, (causal, dO, dL)
+        c = _prefill_compare(Q, K, V, O, L, 1 / math.sqrt(d), causal)
+        assert c.ok(), (causal, c)
 
 
 @pytest.mark.parametrize("causal", [True, False])
@@ -185,24 +183,42 @@ def test_bf16_many_items_per_workgroup(B, H, N, causal):
     fa.fa_fwd(Q, K, V, O, L, causal=causal)
     torch.cuda.synchronize()
     assert not torch.isnan(O).any() and not torch.isnan(L).any()
-    dO, dL = _prefill_compare(Q, K, V, O, L, 1 / math.sqrt(128), causal)
-    assert dO <= BF16_O and dL <= BF16_L, (dO, dL)
+    c = _prefill_compare(Q, K, V, O, L, 1 / math.sqrt(128), causal)
+    assert c.ok(), c
 
 
 def test_bf16_large_values_and_scale():
-    """Scores with a wide spread (values x4, scale 0.05) exercise the running
-    maximum and the alpha rescale across many tiles."""
+    """Scores with a wide spread (values x4, scale 0.05: score std about 9)
+    exercise the running maximum and the alpha rescale across many tiles.
+    These inputs are far from the workloads' N(0,1): rows are peaked, |O|
+    reaches about 16, and V's spread is four times larger, so rounding the
+    probabilities to bf16 for the W V product alone can move O by more than
+    2e-2 where a row has a few comparable dominant weights.  Every element is
+    held to the bound that follows from the kernel's arithmetic
+    (tests/parity_util.py, rounded_w_bound); the flat-bar comparison is
+    printed beside it."""
     fa = _fa()
     _say("bf16 wide scores")
     shape = (1, 2, 777, 128)
+    N = shape[2]
     Q, K, V = (synth.torch_normal(300 + t, shape, "cuda", "bf16", vscale=4.0) for t in range(3))
     O = torch.empty_like(Q)
     L = torch.empty(shape[:3], device="cuda")
     for causal in (False, True):
         fa.fa_fwd(Q, K, V, O, L, causal=causal, scale=0.05)
         torch.cuda.synchronize()
-        dO, dL = _prefill_compare(Q, K, V, O, L, 0.05, causal)
-        assert dO <= 4 * BF16_O and dL <= BF16_L, (causal, dO, dL)
+        c = _prefill_compare(Q, K, V, O, L, 0.05, causal)
+        print("wide scores causal" if causal else "wide scores", c)
+        worst = 0.0
+        for h in range(shape[1]):
+            q, k, v = _host(Q[0, h]), _host(K[0, h]), _host(V[0, h])
+            o_ref, _ = oracle.attention_rows(q, k, v, 0.05, causal=causal)
+            dev, am = oracle.attention_dev_rows(q, k, v, 0.05, causal=causal)
+            n_keys = np.arange(1, N + 1) if causal else np.full(N, N)
+            bound = rounded_w_bound(o_ref, dev, am, n_keys)
+            worst = max(worst, float(np.max(np.abs(_host(O[0, h]) - o_ref) / bound)))
+        print(f"  worst |dO| / arithmetic bound = {worst:.3f}")
+        assert worst <= 1.0 and c.dL <= BF16_L, (causal, worst, c)
 
 
 @pytest.mark.parametrize("N", [1000, 2049])
@@ -211,25 +227,25 @@ def test_bf16_base_moves_in_later_tiles(N):
     KV tiles hold scores far above the first tile's maximum: the running base
     moves mid-row, after U and l have been accumulated, and U and l must be
     rescaled ("Invariant of conditional rescaling").  Such peaked rows make O
-    nearly one row of V, so V is halved (exactly) to keep |O| under 4, where
-    the bf16 output rounding leaves room in the 2e-2 bar: at |O| >= 4 half an
-    ulp of bf16 is already 0.0156, and both forward kernels then measure
-    0.0219 on this input."""
+    nearly one row of V (|O| up to about 4.2 here, where the bf16 output
+    rounding alone takes up to 0.0156 of the 2e-2 bar); O is normalised by the
+    sum of the same bf16-rounded weights that formed U, so a dominant weight's
+    rounding cancels."""
     fa = _fa()
     _say("bf16 base moves in later tiles", N)
     shape = (1, 4, N, 128)
     Q, K, V = (synth.torch_normal(800 + t, shape, "cuda", "f32") for t in range(3))
     ramp = 1.0 + 7.0 * torch.arange(N, device="cuda", dtype=torch.float32) / N
     K = K * ramp[None, None, :, None]
-    V = V * 0.5
     Q, K, V = (t.to(torch.bfloat16) for t in (Q, K, V))
     O = torch.empty_like(Q)
     L = torch.empty(shape[:3], device="cuda")
     for causal in (False, True):
         fa.fa_fwd(Q, K, V, O, L, causal=causal)
         torch.cuda.synchronize()
-        dO, dL = _prefill_compare(Q, K, V, O, L, 1 / math.sqrt(128), causal)
-        assert dO <= BF16_O and dL <= BF16_L, (causal, dO, dL)
+        c = _prefill_compare(Q, K, V, O, L, 1 / math.sqrt(128), causal)
+        print("base moves", N, "causal" if causal else "", c)
+        assert c.ok(), (causal, c)
 
 
 @pytest.mark.parametrize("d", [64, 128])
@@ -256,7 +272,9 @@ def _rows_sample(N, seed):
     return np.unique(np.concatenate([fixed, rng.integers(0, N, 32)]))
 
 
-def test_bf16_prefill_8k_workload_sampled():
+def test_bf16_prefill_8k_workload_all_elements():
+    """The prefill_8k workload in the bench's launch configuration, every
+    head and row against the oracle."""
     fa = _fa()
     cfg = synth.WORKLOADS["prefill_8k"]
     _say("prefill_8k", cfg)
@@ -265,15 +283,16 @@ def test_bf16_prefill_8k_workload_sampled():
     L = torch.empty(Q.shape[:3], device="cuda")
     fa.fa_fwd(Q, K, V, O, L, causal=False)
     torch.cuda.synchronize()
-    rows = _rows_sample(cfg["N"], 1)
-    dO, dL = _prefill_compare(Q, K, V, O, L, 1 / math.sqrt(cfg["d"]), False, rows=rows,
-                              heads=[(0, 0), (0, 7), (0, 18), (0, 31)])
-    print(f"prefill_8k sampled max|dO|={dO:.3e} max|dL|={dL:.3e}")
-    assert dO <= BF16_O and dL <= BF16_L
     assert torch.isfinite(O).all() and torch.isfinite(L).all()
+    c = _prefill_compare(Q, K, V, O, L, 1 / math.sqrt(cfg["d"]), False)
+    print("prefill_8k", c, flush=True)
+    assert c.n == Q.numel()
+    assert c.ok(), c
 
 
-def test_bf16_causal_4k_workload_sampled():
+def test_bf16_causal_4k_workload_all_elements():
+    """The causal_4k workload in the bench's launch configuration, every
+    (b, h) and row against the oracle."""
     fa = _fa()
     cfg = synth.WORKLOADS["causal_4k"]
     _say("causal_4k", cfg)
@@ -282,14 +301,13 @@ def test_bf16_causal_4k_workload_sampled():
     L = torch.empty(Q.shape[:3], device="cuda")
     fa.fa_fwd(Q, K, V, O, L, causal=True)
     torch.cuda.synchronize()
-    rows = _rows_sample(cfg["N"], 2)
-    dO, dL = _prefill_compare(Q, K, V, O, L, 1 / math.sqrt(cfg["d"]), True, rows=rows,
-                              heads=[(0, 0), (1, 5), (2, 17), (3, 31)])
-    print(f"causal_4k sampled max|dO|={dO:.3e} max|dL|={dL:.3e}")
-    assert dO <= BF16_O and dL <= BF16_L
+    assert torch.isfinite(O).all() and torch.isfinite(L).all()
     # causal row 0 sees only key 0: O_0 = V_0 exactly up to output rounding
     assert torch.equal(O[:, :, 0], V[:, :, 0])
-    assert torch.isfinite(O).all() and torch.isfinite(L).all()
+    c = _prefill_compare(Q, K, V, O, L, 1 / math.sqrt(cfg["d"]), True)
+    print("causal_4k", c, flush=True)
+    assert c.n == Q.numel()
+    assert c.ok(), c
 
 
 # --------------------------------------------------------------------------
@@ -308,20 +326,18 @@ def _decode_oracle(q, Kc, Vc, lengths, H, d, b, h, scale, capacity=0):
 
 
 def _decode_compare(q, Kc, Vc, o, lengths, lse=None, pairs=None, scale=None, capacity=0):
+    """Compare o (and lse when given) with the oracle on the given (b, h)
+    pairs (all when None).  Returns a Cmp."""
     B, H, d = q.shape
     scale = scale or 1 / math.sqrt(d)
     pairs = pairs if pairs is not None else [(b, h) for b in range(B) for h in range(H)]
-    dO = dL = 0.0
+    c = Cmp(bf16=True)
     for b, h in pairs:
         o_ref, l_ref = _decode_oracle(q, Kc, Vc, lengths, H, d, b, h, scale, capacity)
-        dO = max(dO, float(np.max(np.abs(_host(o[b, h]) - o_ref))))
+        c.add_o(_host(o[b, h]), o_ref)
         if lse is not None:
-            ld = float(lse[b, h].item())
-            if l_ref == -np.inf:
-                assert ld == -np.inf
-            else:
-                dL = max(dL, abs(ld - l_ref))
-    return dO, dL
+            c.add_l(np.array([float(lse[b, h].item())]), np.array([l_ref]))
+    return c
 
 
 @pytest.mark.parametrize("d", [64, 128])
@@ -343,9 +359,9 @@ def test_decode_small(d, splits):
     lse = torch.empty(B, H, device="cuda")
     fa.fa_decode_ex(q, Kc, Vc, o2, Lkv, ws, lse_out=lse, num_splits=splits)
     torch.cuda.synchronize()
-    dO, _ = _decode_compare(q, Kc, Vc, o, lengths)
-    dO2, dL2 = _decode_compare(q, Kc, Vc, o2, lengths, lse=lse)
-    assert dO <= BF16_O and dO2 <= BF16_O and dL2 <= BF16_L, (dO, dO2, dL2)
+    c = _decode_compare(q, Kc, Vc, o, lengths)
+    c2 = _decode_compare(q, Kc, Vc, o2, lengths, lse=lse)
+    assert c.ok() and c2.ok(), (c, c2)
     assert torch.all(o[3] == 0)  # empty cache -> o = 0
 
 
@@ -363,8 +379,8 @@ def test_decode_padded_layout_and_scale():
     ws = torch.empty(fa.fa_decode_workspace_bytes(B, H, d, 5), dtype=torch.uint8, device="cuda")
     fa.fa_decode_ex(q, Kc, Vc, o, Lkv, ws, lse_out=lse, kv_seq_capacity=cap, num_splits=5, scale=0.3)
     torch.cuda.synchronize()
-    dO, dL = _decode_compare(q, Kc, Vc, o, lengths, lse=lse, scale=0.3, capacity=cap)
-    assert dO <= BF16_O and dL <= BF16_L, (dO, dL)
+    c = _decode_compare(q, Kc, Vc, o, lengths, lse=lse, scale=0.3, capacity=cap)
+    assert c.ok(), c
 
 
 def test_decode_split_invariance_and_prefill_row():
@@ -389,8 +405,8 @@ def test_decode_split_invariance_and_prefill_row():
     for o in outs:
         assert float((o.float() - outs[0].float()).abs().max()) <= 2 * BF16_O
         assert float((o.float() - O[:, :, 100].float()).abs().max()) <= 2 * BF16_O
-    dO, _ = _decode_compare(q, K, V, outs[-1], np.array([N]))
-    assert dO <= BF16_O
+    c = _decode_compare(q, K, V, outs[-1], np.array([N]))
+    assert c.ok(), c
 
 
 def test_decode_32k_workload_all_heads():
@@ -407,13 +423,13 @@ def test_decode_32k_workload_all_heads():
     lse = torch.empty(B, H, device="cuda")
     fa.fa_decode_ex(q, Kc, Vc, o64, Lkv, ws, lse_out=lse, num_splits=64)
     torch.cuda.synchronize()
-    dO, _ = _decode_compare(q, Kc, Vc, o, lengths)
-    dO64, dL64 = _decode_compare(q, Kc, Vc, o64, lengths, lse=lse)
-    print(f"decode_32k max|dO|={dO:.3e} (auto) {dO64:.3e} (64 splits) max|dL|={dL64:.3e}")
-    assert dO <= BF16_O and dO64 <= BF16_O and dL64 <= BF16_L
+    c = _decode_compare(q, Kc, Vc, o, lengths)
+    c64 = _decode_compare(q, Kc, Vc, o64, lengths, lse=lse)
+    print("decode_32k auto:", c, "| 64 splits:", c64)
+    assert c.ok() and c64.ok(), (c, c64)
 
 
-def test_decode_varlen_workload_sampled():
+def test_decode_varlen_workload_all_pairs():
     fa = _fa()
     cfg = synth.WORKLOADS["decode_varlen"]
     q, Kc, Vc, lengths = synth.decode_inputs("decode_varlen", "cuda")
@@ -428,10 +444,10 @@ def test_decode_varlen_workload_sampled():
     fa.fa_decode_ex(q, Kc, Vc, o2, Lkv, ws, lse_out=lse, num_splits=0)
     torch.cuda.synchronize()
     assert torch.equal(o, o2)
-    pairs = [(b, h) for b in range(B) for h in (0, 13, 31)]
-    dO, dL = _decode_compare(q, Kc, Vc, o2, lengths, lse=lse, pairs=pairs)
-    print(f"decode_varlen sampled max|dO|={dO:.3e} max|dL|={dL:.3e}")
-    assert dO <= BF16_O and dL <= BF16_L
+    c = _decode_compare(q, Kc, Vc, o2, lengths, lse=lse)
+    print("decode_varlen (all 256 pairs)", c)
+    assert c.n == q.numel()
+    assert c.ok(), c
     assert torch.isfinite(o.float()).all()
 
 
@@ -451,9 +467,9 @@ def test_bf16_long_sequence_sampled(causal):
     fa.fa_fwd(Q, K, V, O, L, causal=causal)
     torch.cuda.synchronize()
     rows = _rows_sample(shape[2], 3)
-    dO, dL = _prefill_compare(Q, K, V, O, L, 1 / math.sqrt(128), causal, rows=rows, heads=[(0, 0), (0, 1)])
-    print(f"N=65536 causal={causal} max|dO|={dO:.3e} max|dL|={dL:.3e}")
-    assert dO <= BF16_O and dL <= BF16_L
+    c = _prefill_compare(Q, K, V, O, L, 1 / math.sqrt(128), causal, rows=rows, heads=[(0, 0), (0, 1)])
+    print(f"N=65536 causal={causal}", c)
+    assert c.ok(), c
 
 
 @pytest.mark.parametrize("causal", [False, True])
@@ -469,8 +485,8 @@ def test_bf16_many_heads_sampled(causal):
     fa.fa_fwd(Q, K, V, O, L, causal=causal)
     torch.cuda.synchronize()
     heads = [(0, 0), (3, 77), (9, 1), (15, 127)]
-    dO, dL = _prefill_compare(Q, K, V, O, L, 1 / math.sqrt(64), causal, heads=heads)
-    assert dO <= BF16_O and dL <= BF16_L
+    c = _prefill_compare(Q, K, V, O, L, 1 / math.sqrt(64), causal, heads=heads)
+    assert c.ok(), c
     assert torch.isfinite(O).all() and torch.isfinite(L).all()
 
 
@@ -488,6 +504,6 @@ def test_decode_million_token_cache(splits):
     o = torch.empty_like(q)
     fa.fa_decode(q, Kc, Vc, o, Lkv, num_splits=splits)
     torch.cuda.synchronize()
-    dO, _ = _decode_compare(q, Kc, Vc, o, lengths)
-    print(f"decode L=2^20 splits={splits} max|dO|={dO:.3e}")
-    assert dO <= BF16_O
+    c = _decode_compare(q, Kc, Vc, o, lengths)
+    print(f"decode L=2^20 splits={splits}", c)
+    assert c.ok(), c

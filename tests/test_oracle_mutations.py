@@ -228,3 +228,15 @@ def test_backward_dropped_causal_mask_is_caught(monkeypatch):
     orig_scores = bwd._masked_scores
     monkeypatch.setattr(bwd, "_masked_scores", lambda q, k, scale, causal, q_pos: orig_scores(q, k, scale, False, q_pos))
     assert _fails(bpins.test_backward_vs_torch_autograd, 37, 16, 0.3, True)
+
+
+def test_dev_around_zero_instead_of_o_is_caught(monkeypatch):
+    orig = att.attention_dev_rows
+
+    def around_zero(q, k, v, scale, causal=False, q_pos=None):
+        dev, am = orig(q, k, v, scale, causal, q_pos)
+        return am, am
+
+    monkeypatch.setattr(att, "attention_dev_rows", around_zero)
+    monkeypatch.setattr(oracle, "attention_dev_rows", around_zero)
+    assert _fails(pins.test_attention_dev_rows_brute_force_and_closed_forms)

@@ -381,3 +381,52 @@ def test_bf16_inputs_are_exact_in_float64():
     assert np.all(bits & 0xFFFF == 0)
     ref = torch.from_numpy(np.random.default_rng(3).standard_normal(1000, dtype=np.float32)).to(torch.bfloat16)
     np.testing.assert_array_equal(x, ref.float().numpy())
+
+
+def test_attention_dev_rows_brute_force_and_closed_forms():
+    """attention_dev_rows against its definition written as plain loops on a
+    tiny input, and closed forms: one valid key (causal row 0) leaves no
+    spread; two keys with equal scores spread by |v1 - v2| / 2."""
+    rng = np.random.default_rng(31)
+    N, d, dv = 6, 4, 3
+    Q, K, V = rng.standard_normal((N, d)), rng.standard_normal((N, d)), rng.standard_normal((N, dv))
+    for causal in (False, True):
+        dev, am = oracle.attention_dev_rows(Q, K, V, 0.7, causal=causal)
+        for i in range(N):
+            keys = [j for j in range(N) if not causal or j <= i]
+            s = [0.7 * sum(Q[i, t] * K[j, t] for t in range(d)) for j in keys]
+            mx = max(s)
+            e = [math.exp(x - mx) for x in s]
+            tot = sum(e)
+            p = [x / tot for x in e]
+            for c in range(dv):
+                o = sum(pj * V[j, c] for pj, j in zip(p, keys))
+                assert dev[i, c] == pytest.approx(sum(pj * abs(V[j, c] - o) for pj, j in zip(p, keys)), abs=1e-13)
+                assert am[i, c] == pytest.approx(sum(pj * abs(V[j, c]) for pj, j in zip(p, keys)), abs=1e-13)
+        if causal:
+            np.testing.assert_allclose(dev[0], 0.0, atol=1e-15)
+            np.testing.assert_allclose(am[0], np.abs(V[0]), atol=1e-15)
+    v2 = np.array([[1.0, -2.0], [3.0, 5.0]])
+    dev, am = oracle.attention_dev_rows(np.zeros((1, 4)), rng.standard_normal((2, 4)), v2, 1.0)
+    np.testing.assert_allclose(dev[0], [1.0, 3.5], atol=1e-15)
+    np.testing.assert_allclose(am[0], [2.0, 3.5], atol=1e-15)
+
+
+def test_attention_dev_rows_bounds_rounded_probabilities():
+    """The use it is made for: perturbing every probability by a relative
+    amount of at most delta and renormalising moves O by at most
+    delta / (1 - delta) * dev."""
+    rng = np.random.default_rng(32)
+    N, d = 200, 16
+    Q, K, V = (rng.standard_normal((N, d)) * 3 for _ in range(3))
+    O, L = oracle.attention_ref(Q, K, V, 0.4)
+    dev, _ = oracle.attention_dev_rows(Q, K, V, 0.4)
+    P = np.exp(Q @ K.T * 0.4 - L[:, None])
+    delta = 2.0 ** -8
+    worst = 0.0
+    for trial in range(20):
+        Pp = P * (1 + delta * rng.choice([-1.0, 1.0], size=P.shape) * rng.uniform(0.5, 1.0, size=P.shape))
+        Op = (Pp @ V) / Pp.sum(1, keepdims=True)
+        worst = max(worst, float(np.max(np.abs(Op - O) / (delta / (1 - delta) * dev + 1e-300))))
+    assert worst <= 1.0
+    assert worst > 0.05  # the bound is not vacuous
