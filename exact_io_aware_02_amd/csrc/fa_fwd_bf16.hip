@@ -172,7 +172,7 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ K
   // online-softmax base m (raw score units, equal in lanes l and l^32), the
   // per-lane partial l over the lane's keys, and the U^T accumulators
   bf16x8_t qf[D / 16];
-  float m_ref, l_run, lr_run;
+  float m_ref, l_run;
   f32x16_t u[D / 32];
 
   // KV tiles of query tile qt (causal tiles wholly in the future skipped)
@@ -253,7 +253,6 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ K
 
   m_ref = -INFINITY;
   l_run = 0.f;
-  lr_run = 0.f;
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) u[db] = f32x16_t{};
 
@@ -325,13 +324,10 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ K
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) u[db] *= alpha;
     }
-    // W in bf16 for the product; fp32 partial sums for l, which gives L (so
-    // L carries no bf16 rounding), and partial sums of the rounded weights
-    // for lr, which normalises O (so U and its divisor carry the same
-    // rounding of every weight): wb[2c + h] holds key step 2c + h
+    // W in bf16 for the product, fp32 partial sums for l (so l and L carry
+    // no bf16 rounding): wb[2c + h] holds key step 2c + h
     bf16x8_t wb[2 * kKB];
-    float rsp[2 * kKB], rrp[2 * kKB];
-    const bf16x2_t ones = {(__bf16)1.f, (__bf16)1.f};
+    float rsp[2 * kKB];
 #pragma unroll
     for (int cb = 0; cb < kKB; ++cb) {
 #pragma unroll
@@ -342,30 +338,18 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ K
         rsp[2 * cb + h] = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
         wb[2 * cb + h] = bf16x8_t{(__bf16)p[0], (__bf16)p[1], (__bf16)p[2], (__bf16)p[3],
                                  (__bf16)p[4], (__bf16)p[5], (__bf16)p[6], (__bf16)p[7]};
-        float r = 0.f;
-#pragma unroll
-        for (int t = 0; t < 8; t += 2) {
-          const bf16x2_t pr = {wb[2 * cb + h][t], wb[2 * cb + h][t + 1]};
-          r = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, r, false);
-        }
-        rrp[2 * cb + h] = r;
       }
     }
 #pragma unroll
     for (int w = 2 * kKB; w > 1; w >>= 1) {
 #pragma unroll
-      for (int i = 0; i < w / 2; ++i) {
-        rsp[i] += rsp[i + w / 2];
-        rrp[i] += rrp[i + w / 2];
-      }
+      for (int i = 0; i < w / 2; ++i) rsp[i] += rsp[i + w / 2];
     }
     l_run = alpha * l_run + rsp[0];
-    lr_run = alpha * lr_run + rrp[0];
     // keep the compiler from sinking the softmax into the matrix slot
 #pragma unroll
     for (int k = 0; k < 2 * kKB; ++k) keep(wb[k]);
     keep(l_run);
-    keep(lr_run);
     end_slot(sa);
 
     // -- matrix slot of tile j (MFMA): U^T += V_j^T W^T, then the scores of
@@ -404,7 +388,7 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ K
   wg_barrier();
   };
 
-  // ---- end of an item: O = U / lr, L = m * scale + ln l.  Called after
+  // ---- end of an item: O = U / l, L = m * scale + ln l.  Called after
   // the item's last barrier, when no wavefront reads the K/V tiles any more:
   // O goes through the wavefront's own 32 padded rows of that area, in
   // which each lane writes its row's pieces; whole rows then leave with one
@@ -415,8 +399,7 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ K
   const int qw0 = qt * kFwdBR + wave * 32;
   const int qrow = qw0 + l32;
   const float l_tot = pair_sum(l_run);
-  const float lr_tot = pair_sum(lr_run);
-  const float inv = lr_tot > 0.f ? 1.f / lr_tot : 0.f;
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   char LDS_AS* const stage = lds + wave * 32 * T::kStride;
   // the lane index as an opaque copy, so that the lane-dependent addresses
   // below are formed here and not hoisted out of the item loop, where they

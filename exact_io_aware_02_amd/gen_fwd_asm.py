@@ -24,7 +24,7 @@ register files; written out, every value has one home:
   v[0:127]    score tiles S_A, S_B: s[cb][qb] = 16 VGPRs at (2 cb + qb) * 16
   v[128:191]  probability tiles W_A, W_B: w[qb][ks] = 4 VGPRs at (4 qb + ks) * 4
   v[192:207]  softmax temporaries
-  v[208:224]  per-row state (base m, partial l and its rounded twin, alpha, ...)
+  v[208:223]  per-row state (base m, partial l, alpha, ...)
 
 Each tile step j (64 keys) is one straight-line stream that overlaps, inside
 the wavefront, U += V_{j-1}^T W_{j-1}^T and S_{j+1} = K_{j+1} Q^T on the
@@ -68,21 +68,14 @@ W_BUF = [128, 160]           # VGPR base of W_A, W_B
 TMP0 = 192                   # 16 temporaries v[192:207]
 ST = 208                     # state registers v[208:223]
 V_M = [ST + 0, ST + 1]       # base m per query block (raw score units)
-V_L = [ST + 2, ST + 3]       # partial l per query block (this lane's keys): fp32 weights, for L
+V_L = [ST + 2, ST + 3]       # partial l per query block (this lane's keys)
 V_MC = [ST + 4, ST + 5]      # m * c (VGPR banks 0, 1)
 V_AL = [ST + 6, ST + 7]      # alpha
 V_MX = [ST + 8, ST + 9]      # tile max
 V_NINF = ST + 10             # -inf
 V_THR = [ST + 11, ST + 12]   # mask thresholds
+V_T = ST + 13                # scratch
 V_MC2 = [ST + 14, ST + 15]   # m * c again, in VGPR banks 2, 3
-# partial l per query block summed from the bf16-rounded weights that enter
-# the W V product, for O = U / l (ST + 16 is one register past the block)
-V_LR = [ST + 13, ST + 16]
-# per query block two chains of the tile's rounded-weight sums; both homes
-# are free while a step's softmax runs (the mask thresholds are used before
-# it, the tile max only before the weights are formed)
-V_RS = [[ST + 11, ST + 8], [ST + 12, ST + 9]]
-NVGPR = ST + 17              # v[0:NVGPR-1] are the generated code's
 FRAG0 = 192                  # AGPR fragment slots a[192:255]
 NSLOT = 16
 LOOKAHEAD = 6
@@ -105,10 +98,9 @@ S_M0 = 58       # the caller's M0, restored at the end
 S_C = 70        # c = scale * log2(e)
 S_THETA = 71    # rescale threshold (raw score units)
 S_256 = 72      # 2^8 as fp32
-S_ONES = 73     # bf16 pair (1, 1): v_dot2 with it sums a packed pair
 S_RK = 60       # s[60:63]: resource of the K tile being loaded
 S_RV = 64       # s[64:67]: resource of the V tile being loaded
-SGPR_CLOBBERS = list(range(40, 59)) + list(range(60, 68)) + [S_C, S_THETA, S_256, S_ONES]
+SGPR_CLOBBERS = list(range(40, 59)) + list(range(60, 68)) + [S_C, S_THETA, S_256]
 
 
 def kfrag_reads(slot, buf, cb, ds):
@@ -225,18 +217,14 @@ def softmax_ops(sbuf, wbuf, fast=False):
     ops += exp_ops(sb, wbuf, pair_tmp, psum)
     for qb in range(2):
         ops.append(f"v_fma_f32 v{V_L[qb]}, v{V_AL[qb]}, v{V_L[qb]}, v{psum[4 * qb]}")
-        ops.append(f"v_fma_f32 v{V_LR[qb]}, v{V_AL[qb]}, v{V_LR[qb]}, v{V_RS[qb][0]}")
     return ops
 
 
 def exp_ops(sb, wbuf, pair_tmp, psum):
     """W = exp2(c S - c m) for a score tile: per pair of scores two FMAs, two
     exponentials (each read at least one instruction later), two adds into
-    the fp32 partial sum of the pair's 8-key group, one bf16 pack, and one
-    v_dot2 of the packed pair with (1, 1) into a sum of the rounded weights;
-    the two query blocks alternate.  Leaves the per-lane tile sums in psum[0],
-    psum[4] (fp32 weights) and V_RS[qb][0] (the bf16 weights the product
-    uses)."""
+    the partial sum of the pair's 8-key group, one bf16 pack; the two query
+    blocks alternate.  Leaves the per-lane tile sums in psum[0], psum[4]."""
     ops = []
     seqs = {0: [], 1: []}
     k_pair = 0
@@ -250,7 +238,6 @@ def exp_ops(sb, wbuf, pair_tmp, psum):
                 a, b = pair_tmp[k_pair % 4]
                 k_pair += 1
                 ps = psum[4 * qb + ks]
-                rs = V_RS[qb][k & 1]
                 seqs[qb] += [
                     f"v_fma_f32 v{a}, v{src}, s{S_C}, -v{mcx}",
                     f"v_fma_f32 v{b}, v{src + 1}, s{S_C}, -v{mcx}",
@@ -259,19 +246,15 @@ def exp_ops(sb, wbuf, pair_tmp, psum):
                     f"v_add_f32 v{ps}, 0, v{a}" if k == 0 else f"v_add_f32 v{ps}, v{ps}, v{a}",
                     f"v_add_f32 v{ps}, v{ps}, v{b}",
                     f"v_cvt_pk_bf16_f32 v{w + k}, v{a}, v{b}",
-                    (f"v_dot2_f32_bf16 v{rs}, s{S_ONES}, v{w + k}, 0" if ks == 0 and k < 2
-                     else f"v_dot2_f32_bf16 v{rs}, s{S_ONES}, v{w + k}, v{rs}"),
                 ]
-    n = 8
-    for i in range(0, len(seqs[0]), n):
-        ops += seqs[0][i:i + n] + seqs[1][i:i + n]
+    for i in range(0, len(seqs[0]), 7):
+        ops += seqs[0][i:i + 7] + seqs[1][i:i + 7]
     for qb in range(2):
         p = psum[4 * qb:4 * qb + 4]
         ops += [f"v_add_f32 v{p[0]}, v{p[0]}, v{p[1]}", f"v_add_f32 v{p[2]}, v{p[2]}, v{p[3]}"]
     for qb in range(2):
         p = psum[4 * qb:4 * qb + 4]
         ops.append(f"v_add_f32 v{p[0]}, v{p[0]}, v{p[2]}")
-        ops.append(f"v_add_f32 v{V_RS[qb][0]}, v{V_RS[qb][0]}, v{V_RS[qb][1]}")
     return ops
 
 
@@ -556,8 +539,6 @@ def step(st, parity, causal, kind, label):
         st.emit(f"s_cbranch_scc1 {label}_slow_%=")
         st.emit(f"v_add_f32 v{V_L[0]}, v{V_L[0]}, v{t0}")
         st.emit(f"v_add_f32 v{V_L[1]}, v{V_L[1]}, v{t1}")
-        st.emit(f"v_add_f32 v{V_LR[0]}, v{V_LR[0]}, v{V_RS[0][0]}")
-        st.emit(f"v_add_f32 v{V_LR[1]}, v{V_LR[1]}, v{V_RS[1][0]}")
         st.emit(f"s_branch {label}_done_%=")
         st.emit(f"{label}_slow_%=:")
         for ins in softmax_ops(j_odd, j_odd):
@@ -614,13 +595,11 @@ def item_asm(causal):
     e(f"v_readfirstlane_b32 s{S_C}, %[c]")
     e(f"v_readfirstlane_b32 s{S_THETA}, %[theta]")
     e(f"s_mov_b32 s{S_256}, 0x43800000")
-    e(f"s_mov_b32 s{S_ONES}, 0x3f803f80")
     e(f"v_mov_b32 v{V_NINF}, 0xff800000")
     e(f"v_mov_b32 v{V_M[0]}, 0xff800000")
     e(f"v_mov_b32 v{V_M[1]}, 0xff800000")
-    for qb in range(2):
-        e(f"v_mov_b32 v{V_L[qb]}, 0")
-        e(f"v_mov_b32 v{V_LR[qb]}, 0")
+    e(f"v_mov_b32 v{V_L[0]}, 0")
+    e(f"v_mov_b32 v{V_L[1]}, 0")
     # the first item of a workgroup loads Q (rows past N read as zeros; query
     # block 1 is 32 rows, 8 KiB, further), K_0 and K_1 itself
     e("s_cmp_eq_u32 %[pre], 0")
@@ -697,24 +676,16 @@ def item_asm(causal):
     st.block(pv_frags(0, 0), [], groups=prefetch_groups())
     e("L_done_%=:")
     # epilogue: every wavefront done with the V buffers (the next item loads
-    # V_0 at once); O = U / l into this wavefront's 64 staging rows, with l
-    # the sum of the same bf16-rounded weights that formed U, so that the
-    # numerator and the denominator carry one rounding of each weight (l and
-    # its rounded twin summed over the lane pair first; the fp32 l gives L)
+    # V_0 at once); O = U / l into this wavefront's 64 staging rows (l summed
+    # over the lane pair first)
     e("s_waitcnt lgkmcnt(0)")
     e("s_barrier")
     for qb in range(2):
-        for k, r in enumerate((V_L[qb], V_LR[qb])):
-            e(f"v_mov_b32 v{TMP0 + 2 * qb + k}, v{r}")
-    e("s_nop 1")
-    for qb in range(2):
-        for k, r in enumerate((V_L[qb], V_LR[qb])):
-            e(f"v_permlane32_swap_b32 v{r}, v{TMP0 + 2 * qb + k}")
-    for qb in range(2):
-        for k, r in enumerate((V_L[qb], V_LR[qb])):
-            e(f"v_add_f32 v{r}, v{r}, v{TMP0 + 2 * qb + k}")
-    for qb in range(2):
-        e(f"v_rcp_f32 v{V_AL[qb]}, v{V_LR[qb]}")
+        e(f"v_mov_b32 v{V_T}, v{V_L[qb]}")
+        e("s_nop 1")
+        e(f"v_permlane32_swap_b32 v{V_L[qb]}, v{V_T}")
+        e(f"v_add_f32 v{V_L[qb]}, v{V_L[qb]}, v{V_T}")
+        e(f"v_rcp_f32 v{V_AL[qb]}, v{V_L[qb]}")
     e("s_nop 15")
     e("s_nop 15")
     e("s_nop 15")
@@ -758,7 +729,7 @@ def item_asm(causal):
 
 
 def clobbers():
-    v = [f'"v{i}"' for i in range(0, NVGPR)]
+    v = [f'"v{i}"' for i in range(0, ST + 16)]
     a = [f'"a{i}"' for i in range(256)]
     s = [f'"s{i}"' for i in SGPR_CLOBBERS]
     return ", ".join(v + a + s + ['"vcc"', '"scc"', '"memory"'])

@@ -91,7 +91,7 @@ def test_register_homes_are_disjoint(program):
         "S": set(range(g.S_BUF[0], g.S_BUF[1] + 64)),
         "W": set(range(g.W_BUF[0], g.W_BUF[1] + 32)),
         "tmp": set(range(g.TMP0, g.TMP0 + 16)),
-        "state": set(range(g.ST, g.NVGPR)),
+        "state": set(range(g.ST, g.ST + 16)),
     }
     names = list(vhomes)
     for i, a in enumerate(names):

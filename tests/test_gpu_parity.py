@@ -187,16 +187,31 @@ def test_bf16_many_items_per_workgroup(B, H, N, causal):
     assert c.ok(), c
 
 
+def _bound_compare(Q, K, V, O, L, scale, causal):
+    """(max over elements of |GPU - oracle| / the bound from the arithmetic,
+    the flat-bar comparison) for every head and row."""
+    B, H, N, d = Q.shape
+    c = _prefill_compare(Q, K, V, O, L, scale, causal)
+    worst = 0.0
+    n_keys = np.arange(1, N + 1) if causal else np.full(N, N)
+    for b in range(B):
+        for h in range(H):
+            q, k, v = _host(Q[b, h]), _host(K[b, h]), _host(V[b, h])
+            o_ref, _ = oracle.attention_rows(q, k, v, scale, causal=causal)
+            _, am = oracle.attention_dev_rows(q, k, v, scale, causal=causal)
+            bound = rounded_w_bound(o_ref, am, n_keys)
+            worst = max(worst, float(np.max(np.abs(_host(O[b, h]) - o_ref) / bound)))
+    return worst, c
+
+
 def test_bf16_large_values_and_scale():
     """Scores with a wide spread (values x4, scale 0.05: score std about 9)
     exercise the running maximum and the alpha rescale across many tiles.
-    These inputs are far from the workloads' N(0,1): rows are peaked, |O|
-    reaches about 16, and V's spread is four times larger, so rounding the
-    probabilities to bf16 for the W V product alone can move O by more than
-    2e-2 where a row has a few comparable dominant weights.  Every element is
-    held to the bound that follows from the kernel's arithmetic
-    (tests/parity_util.py, rounded_w_bound); the flat-bar comparison is
-    printed beside it."""
+    These inputs are far from the workloads' N(0,1): rows are peaked and |O|
+    reaches about 16, so rounding the probabilities to bf16 for the W V
+    product alone can move O by more than 2e-2.  Every element is held to the
+    bound that follows from the kernel's arithmetic (tests/parity_util.py,
+    rounded_w_bound); the flat-bar comparison is printed beside it."""
     fa = _fa()
     _say("bf16 wide scores")
     shape = (1, 2, 777, 128)
@@ -207,17 +222,8 @@ def test_bf16_large_values_and_scale():
     for causal in (False, True):
         fa.fa_fwd(Q, K, V, O, L, causal=causal, scale=0.05)
         torch.cuda.synchronize()
-        c = _prefill_compare(Q, K, V, O, L, 0.05, causal)
-        print("wide scores causal" if causal else "wide scores", c)
-        worst = 0.0
-        for h in range(shape[1]):
-            q, k, v = _host(Q[0, h]), _host(K[0, h]), _host(V[0, h])
-            o_ref, _ = oracle.attention_rows(q, k, v, 0.05, causal=causal)
-            dev, am = oracle.attention_dev_rows(q, k, v, 0.05, causal=causal)
-            n_keys = np.arange(1, N + 1) if causal else np.full(N, N)
-            bound = rounded_w_bound(o_ref, dev, am, n_keys)
-            worst = max(worst, float(np.max(np.abs(_host(O[0, h]) - o_ref) / bound)))
-        print(f"  worst |dO| / arithmetic bound = {worst:.3f}")
+        worst, c = _bound_compare(Q, K, V, O, L, 0.05, causal)
+        print("wide scores causal" if causal else "wide scores", c, f"| worst |dO|/bound = {worst:.3f}")
         assert worst <= 1.0 and c.dL <= BF16_L, (causal, worst, c)
 
 
@@ -226,11 +232,13 @@ def test_bf16_base_moves_in_later_tiles(N):
     """Keys grow along the sequence (key j scaled by 1 + 7 j / N), so later
     KV tiles hold scores far above the first tile's maximum: the running base
     moves mid-row, after U and l have been accumulated, and U and l must be
-    rescaled ("Invariant of conditional rescaling").  Such peaked rows make O
-    nearly one row of V (|O| up to about 4.2 here, where the bf16 output
-    rounding alone takes up to 0.0156 of the 2e-2 bar); O is normalised by the
-    sum of the same bf16-rounded weights that formed U, so a dominant weight's
-    rounding cancels."""
+    rescaled ("Invariant of conditional rescaling").  The rows are peaked, O
+    is nearly one row of V (|O| up to about 4.2), and a dominant weight
+    relative to a base left below the row maximum is not exactly 1: its bf16
+    rounding moves O by up to 2^-8 |O| on top of the output rounding (up to
+    0.0156 at |O| >= 4).  Every element is held to the bound that follows
+    from the kernel's arithmetic (tests/parity_util.py, rounded_w_bound), L
+    to 2e-3; the flat-bar comparison is printed beside it."""
     fa = _fa()
     _say("bf16 base moves in later tiles", N)
     shape = (1, 4, N, 128)
@@ -243,9 +251,9 @@ def test_bf16_base_moves_in_later_tiles(N):
     for causal in (False, True):
         fa.fa_fwd(Q, K, V, O, L, causal=causal)
         torch.cuda.synchronize()
-        c = _prefill_compare(Q, K, V, O, L, 1 / math.sqrt(128), causal)
-        print("base moves", N, "causal" if causal else "", c)
-        assert c.ok(), (causal, c)
+        worst, c = _bound_compare(Q, K, V, O, L, 1 / math.sqrt(128), causal)
+        print("base moves", N, "causal" if causal else "", c, f"| worst |dO|/bound = {worst:.3f}")
+        assert worst <= 1.0 and c.dL <= BF16_L, (causal, worst, c)
 
 
 @pytest.mark.parametrize("d", [64, 128])

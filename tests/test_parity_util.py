@@ -70,19 +70,32 @@ def test_cmp_l_and_empty_rows():
 
 def test_rounded_w_bound_covers_an_emulated_kernel():
     """An emulation of the kernel's arithmetic in numpy -- fp32 weights
-    rounded to bf16, O normalised by the sum of the rounded weights, bf16
-    output -- stays within the bound on wide scores."""
+    relative to a base below the row maximum (as conditional rescaling
+    leaves it), rounded to bf16 for the product, O normalised by the fp32
+    sum, bf16 output -- stays within the bound on peaked rows, where the flat
+    2e-2 bar does not hold."""
     import oracle
 
     rng = np.random.default_rng(3)
     N, d = 300, 64
     Q, K, V = (bf16_rne64(rng.standard_normal((N, d)) * 4) for _ in range(3))
     O, L = oracle.attention_ref(Q, K, V, 0.05)
-    dev, am = oracle.attention_dev_rows(Q, K, V, 0.05)
+    _, am = oracle.attention_dev_rows(Q, K, V, 0.05)
     s = Q @ K.T * 0.05
-    w = np.exp(s - s.max(1, keepdims=True)).astype(np.float32).astype(np.float64)
+    base = s.max(1, keepdims=True) - rng.uniform(0, 8 * np.log(2), size=(N, 1))
+    w = np.exp(s - base).astype(np.float32).astype(np.float64)
     wb = bf16_rne64(w)
-    o_k = bf16_rne64((wb @ V) / wb.sum(1, keepdims=True))
-    bound = rounded_w_bound(O, dev, am, N)
+    o_k = bf16_rne64((wb @ V) / w.sum(1, keepdims=True))
+    bound = rounded_w_bound(O, am, N)
     assert np.all(np.abs(o_k - O) <= bound)
     assert np.max(np.abs(o_k - O)) > BF16_O  # the flat bar would not hold here
+
+
+def test_excess_of_a_power_of_two_output():
+    """-4.0127 rounds to -4.0 (spacing 2^-5 in [4, 8)): the stored -4.0 is the
+    correctly rounded value, so it shows no kernel error."""
+    c = Cmp()
+    c.add_o(np.array([-4.0]), np.array([-4.0127]))
+    assert c.d_rne == 0.0 and c.excess <= 0.0
+    c.add_o(np.array([4.0]), np.array([3.998]))
+    assert c.excess <= 0.0
