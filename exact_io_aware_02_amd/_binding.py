@@ -69,6 +69,8 @@ def _load():
         "fa_bwd_workspace_bytes": (Z, [I, I, I]),
         "fa_decode_ex": (I, [P, P, P, P, P, I, I, P, I, I, I, F, P, Z, P]),
         "fa_decode_workspace_bytes": (Z, [I, I, I, I]),
+        "fa_decode_noalloc": (I, [P, P, P, P, P, I, I, P, I, I, I, F, P]),
+        "fa_decode_noalloc_scratch_bytes": (Z, []),
         "fa_decode_paged": (I, [P, P, P, P, P, I, I, P, I, P, I, I, I, I, F, P, Z, P]),
         "fa_decode_paged_splits": (I, [I, I, I, I, I]),
         "fa_fwd_plan": (I, [I, I, I, I, I, ctypes.POINTER(fa_fwd_plan_t)]),
@@ -97,6 +99,8 @@ EXPORTED = (
     "fa_decode",
     "fa_decode_ex",
     "fa_decode_workspace_bytes",
+    "fa_decode_noalloc",
+    "fa_decode_noalloc_scratch_bytes",
     "fa_decode_paged",
     "fa_decode_paged_splits",
     "fa_fwd_plan",
@@ -273,6 +277,26 @@ def fa_decode_ex(q, Kcache, Vcache, o, Lkv, workspace, lse_out=None, kv_seq_capa
     _check(lib.fa_decode_ex(_ptr(q), _ptr(Kcache), _ptr(Vcache), _ptr(o), _ptr(lse_out), B, H,
                             _ptr(Lkv), int(kv_seq_capacity), d, int(num_splits), float(scale),
                             _ptr(workspace), nbytes, _stream_ptr(stream)))
+    return o, lse_out
+
+
+def fa_decode_noalloc_scratch_bytes():
+    return lib.fa_decode_noalloc_scratch_bytes()
+
+
+def fa_decode_noalloc(q, Kcache, Vcache, o, Lkv, lse_out=None, kv_seq_capacity=0, num_splits=0, scale=None,
+                      stream=None):
+    """fa_decode_ex with the partials in the library's static per-device
+    scratch: allocates nothing (calls that overlap on one device race)."""
+    import torch
+
+    B, H, d = _decode_shapes(q, Kcache, Vcache, o, Lkv)
+    if lse_out is not None:
+        _expect(lse_out, torch.float32, (B, H), "lse_out")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    _check(lib.fa_decode_noalloc(_ptr(q), _ptr(Kcache), _ptr(Vcache), _ptr(o), _ptr(lse_out), B, H, _ptr(Lkv),
+                                 int(kv_seq_capacity), d, int(num_splits), float(scale), _stream_ptr(stream)))
     return o, lse_out
 
 

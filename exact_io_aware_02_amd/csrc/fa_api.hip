@@ -236,6 +236,42 @@ int internal_workspace(size_t need, hipStream_t hs, void** out) {
   return FA_OK;
 }
 
+// Scratch of the allocation-free decode (fa_decode_noalloc): the split
+// partials live in this array instead of a workspace.  Every device the
+// library runs on holds its own copy until the process ends; host code uses
+// only the per-device address hipGetSymbolAddress returns for it (the
+// array's name on the host is a stand-in, not a device address).  Calls on
+// one device share its copy: calls that may overlap on a device race.  The
+// split kernel writes every partial the combine reads (an empty chunk writes
+// O = 0, lse = -inf), so nothing needs clearing between calls.
+constexpr size_t kNoAllocScratchBytes = (size_t)4 << 20;
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+std::mutex g_scratch_mu;
+std::map<int, void*> g_scratch;  // device -> address of its scratch copy
+
+// Address of the current device's scratch, looked up once per device (with
+// that device current).  Allocates nothing.
+int noalloc_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  auto it = g_scratch.find(dev);
+  if (it == g_scratch.end()) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr) {
+      (void)hipGetLastError();
+      return e != hipSuccess ? hip_fail(e, "hipGetSymbolAddress(scratch)")
+                             : fail(FA_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    }
+    it = g_scratch.emplace(dev, p).first;
+  }
+  *out = it->second;
+  return FA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -409,6 +445,31 @@ int fa_decode_ex(const void* q, const void* Kcache, const void* Vcache, void* o,
     return fail(FA_ERR_INVALID_ARG, "workspace overlaps q or o");
   return decode_common(q, Kcache, Vcache, o, lse_out, B, H, Lkv, kv_seq_capacity, d, S, scale,
                        workspace, static_cast<hipStream_t>(stream));
+}
+
+size_t fa_decode_noalloc_scratch_bytes(void) { return kNoAllocScratchBytes; }
+
+int fa_decode_noalloc(const void* q, const void* Kcache, const void* Vcache, void* o, float* lse_out,
+                      int B, int H, const int32_t* Lkv, int kv_seq_capacity, int d, int num_splits,
+                      float scale, void* stream) {
+  int st = check_decode(q, Kcache, Vcache, o, lse_out, B, H, Lkv, kv_seq_capacity, d, num_splits, scale);
+  if (st != FA_OK) return st;
+  int S = num_splits;
+  if (S == 0) {
+    int cus = 0;
+    if ((st = cu_count(&cus)) != FA_OK) return st;
+    S = auto_splits(B, H, cus);
+  }
+  const size_t need = ws_bytes(B, H, d, S);
+  if (need > kNoAllocScratchBytes)
+    return fail(FA_ERR_WORKSPACE,
+                "fa_decode_noalloc: %d x %d x %d partials need %zu bytes, above its %zu-byte scratch "
+                "(use fewer splits, or fa_decode_ex with a workspace)",
+                B, H, S, need, kNoAllocScratchBytes);
+  void* ws = nullptr;
+  if ((st = noalloc_scratch(&ws)) != FA_OK) return st;
+  return decode_common(q, Kcache, Vcache, o, lse_out, B, H, Lkv, kv_seq_capacity, d, S, scale, ws,
+                       static_cast<hipStream_t>(stream));
 }
 
 int fa_decode_paged(const void* q, const void* Kpool, const void* Vpool, void* o, float* lse_out,

@@ -181,6 +181,29 @@ int fa_decode_ex(const void* q, const void* Kcache, const void* Vcache, void* o,
                  int num_splits, float scale, void* workspace, size_t workspace_bytes,
                  void* stream);
 
+/*
+ * fa_decode_noalloc -- fa_decode_ex without a workspace argument and without
+ * any allocation, for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ *   q, Kcache, Vcache, o, lse_out, Lkv, kv_seq_capacity, num_splits, scale :
+ *             as in fa_decode_ex
+ * The split partials go to a static device array inside the library, one per
+ * device, of fa_decode_noalloc_scratch_bytes() bytes (4 MiB: for example
+ * B * H * num_splits up to 8128 partials at d = 128), held until the process
+ * ends.  A request whose partials (fa_decode_workspace_bytes) exceed it is
+ * rejected with FA_ERR_WORKSPACE before anything is enqueued.  Every call on
+ * a device shares that device's array: calls that may overlap on one device
+ * (concurrent streams, other host threads) race and must be ordered by the
+ * caller.  Results are identical to fa_decode_ex with the same arguments.
+ * Errors: as fa_decode_ex.
+ */
+int fa_decode_noalloc(const void* q, const void* Kcache, const void* Vcache, void* o, float* lse_out,
+                      int B, int H, const int32_t* Lkv, int kv_seq_capacity, int d, int num_splits,
+                      float scale, void* stream);
+
+/* Size in bytes of fa_decode_noalloc's per-device scratch. */
+size_t fa_decode_noalloc_scratch_bytes(void);
+
 /* Workspace bytes fa_decode_ex needs; num_splits = 0 resolves the automatic
  * count on the current device.  Returns 0 for invalid arguments. */
 size_t fa_decode_workspace_bytes(int B, int H, int d, int num_splits);

@@ -125,6 +125,25 @@ def test_decode_ex_rejects_bad_workspace_and_capacity():
     assert "too small" in fa.last_error()
 
 
+def test_decode_noalloc_rejects_before_any_hip_call():
+    """The allocation-free decode validates like fa_decode_ex and rejects a
+    request whose partials exceed its static scratch, all on the host (an
+    explicit split count needs no device query)."""
+    fa = _fa()
+    lib = fa.lib
+    assert lib.fa_decode_noalloc_scratch_bytes() == 4 << 20
+    args = (A, 2 * A, 3 * A, 4 * A, None)
+    ok = (2, 4, 5 * A, 0, 128)
+    assert lib.fa_decode_noalloc(None, *args[1:], *ok, 8, ctypes.c_float(0.1), None) == -1
+    assert lib.fa_decode_noalloc(*args, *ok, 8, ctypes.c_float(0.0), None) == -1
+    assert lib.fa_decode_noalloc(*args, 2, 4, 5 * A, 0, 100, 8, ctypes.c_float(0.1), None) == -2
+    # 64 x 64 x 64 partials of 129 floats: far above 4 MiB
+    assert lib.fa_decode_noalloc(*args, 64, 64, 5 * A, 0, 128, 64, ctypes.c_float(0.1), None) == -5
+    assert "scratch" in fa.last_error()
+    # the largest request that fits at d = 128: 8128 partials
+    assert fa.fa_decode_workspace_bytes(8128, 1, 128, 1) <= 4 << 20 < fa.fa_decode_workspace_bytes(8129, 1, 128, 1)
+
+
 def test_decode_workspace_formula():
     fa = _fa()
     for B, H, d, S in [(1, 32, 128, 64), (8, 32, 128, 8), (3, 5, 64, 7)]:
