@@ -50,6 +50,8 @@ def _regs(text):
             out.add((kind, int(one)))
         else:
             out.update((kind, r) for r in range(int(lo), int(hi) + 1))
+    if re.search(r"\bvcc\b", text):
+        out.add(("s", "vcc"))
     return out
 
 
@@ -107,6 +109,8 @@ def test_writes_stay_inside_the_clobbers(program):
         m = re.fullmatch(r"([vas])(\d+)", name)
         if m:
             clob.add((m.group(1), int(m.group(2))))
+        elif name == "vcc":
+            clob.add(("s", "vcc"))
     for line in prog:
         op, dst, _ = _parse(line)
         if "%[" in line.split(",")[0]:
@@ -265,6 +269,199 @@ def test_prefetch_wait_counts_only_later_instructions(program):
     assert f"s_waitcnt vmcnt({g.VM_AFTER_PREFETCH})" in prog
     # the first item of a workgroup waits for all but V_0 (4 or 5 loads)
     assert "s_waitcnt vmcnt(4)" in prog
+
+
+class _Machine:
+    """Symbolic execution of one item's program, enough to follow the LDS
+    buffers: the scalar arithmetic and branches that choose tiles and
+    buffers, the buffer->LDS loads (which tile of which item lands in which
+    buffer), the fragment reads and the MFMAs that consume them.  All four
+    wavefronts run the same program, so a load is visible to every wavefront
+    at the first barrier after this wavefront has waited for it."""
+
+    def __init__(self, g, n, pre, mem, item):
+        self.g, self.n, self.mem, self.item = g, n, mem, item
+        self.vregion = g.KV_LDS[2]          # V buffers follow the K buffers
+        self.ops = {"%[n]": n, "%[pre]": pre, "%[wbase]": 0, "%[wave]": 0,
+                    "%[kb]": 0, "%[vb]": self.vregion, "%[hb]": n * 16384, "%[nhb]": 1 << 24,
+                    "%[klo]": 0, "%[vlo]": 0, "%[nklo]": 1 << 28, "%[nvlo]": 1 << 28, "%[khi]": 0, "%[vhi]": 0,
+                    "%[nkhi]": 0, "%[nvhi]": 0, "%[n_keys]": 64 * n, "%[qw0]": 0, "%[c]": 0, "%[theta]": 0}
+        self.s = {}
+        self.v = {}
+        self.slots = {}   # AGPR slot -> tag of the data read into it
+        self.fin = False
+        self.barriers = 0      # the item's first block (S_0 = K_0 Q^T) follows its first barrier
+        self.errors = []
+
+    def val(self, x):
+        x = x.strip()
+        if x in self.ops:
+            return self.ops[x]
+        if x == "m0":
+            return getattr(self, "m0", 0)
+        if x.startswith("s") and x[1:].isdigit():
+            return self.s.get(int(x[1:]), 0)
+        return int(x, 0)
+
+    def run(self, prog):
+        labels = {ln[:-1]: i for i, ln in enumerate(prog) if ln.endswith(":")}
+        pc, scc, steps = 0, 0, 0
+        while pc < len(prog):
+            steps += 1
+            assert steps < 200000
+            ln = prog[pc]
+            pc += 1
+            if ln.endswith(":"):
+                continue
+            op, _, rest = ln.partition(" ")
+            args = [x.strip() for x in rest.split(",")] if rest else []
+            if op in ("s_mov_b32", "s_add_u32", "s_sub_u32", "s_mul_i32", "s_lshl_b32", "s_cselect_b32", "s_addc_u32") \
+                    and args[0].startswith("s") and args[0][1:].isdigit():
+                d = int(args[0][1:])
+                if op == "s_mov_b32":
+                    r = self.val(args[1])
+                elif op == "s_add_u32":
+                    r = self.val(args[1]) + self.val(args[2])
+                elif op == "s_sub_u32":
+                    r = self.val(args[1]) - self.val(args[2])
+                    scc = int(r < 0)
+                elif op == "s_mul_i32":
+                    r = self.val(args[1]) * self.val(args[2])
+                elif op == "s_lshl_b32":
+                    r = self.val(args[1]) << self.val(args[2])
+                elif op == "s_cselect_b32":
+                    r = self.val(args[1]) if scc else self.val(args[2])
+                else:
+                    r = self.val(args[1])
+                self.s[d] = r
+            elif op == "s_add_u32" and args[0] == "m0":
+                self.m0 = self.val(args[1]) + self.val(args[2])
+            elif op.startswith("s_cmp_"):
+                a_, b_ = self.val(args[0]), self.val(args[1])
+                scc = int({"eq": a_ == b_, "lg": a_ != b_, "lt": a_ < b_, "gt": a_ > b_, "ge": a_ >= b_}[op[6:8]])
+            elif op == "s_cbranch_scc1":
+                if scc:
+                    pc = labels[args[0]]
+            elif op == "s_cbranch_scc0":
+                if not scc:
+                    pc = labels[args[0]]
+            elif op == "s_branch":
+                pc = labels[args[0]]
+            elif op == "v_add_u32" and args[1].startswith("s") and args[2] in ("%[kb]", "%[vb]"):
+                self.v[int(args[0][1:])] = self.val(args[1]) + self.ops[args[2]]
+            elif op == "s_waitcnt" and "vmcnt" in rest:
+                k = int(rest.split("vmcnt(")[1].split(")")[0])
+                self.mem.wait(k)
+            elif op == "s_barrier":
+                self.mem.barrier()
+                self.barriers += 1
+            elif op == "buffer_load_dwordx4" and rest.endswith("lds"):
+                r = int(args[1][2:].split(":")[0])
+                base = self.s[r]
+                item = self.item + (base >> 28)
+                tile = (base & ((1 << 28) - 1)) >> 14
+                kind = "K" if self.m0 < self.vregion else "V"
+                region = 0 if kind == "K" else self.vregion
+                buf = (self.m0 - region) // self.g.TILE
+                assert self.m0 % 1024 == 0 and 0 <= buf < 3, (ln, self.m0)
+                self.mem.load((kind, buf), (kind, item, tile))
+            elif op.startswith("buffer_load") or op.startswith("buffer_store"):
+                self.mem.vmem()
+            elif op.startswith("ds_read") and ("%[kb]" in ln or "%[vb]" in ln):
+                base = self.ops[args[1].split()[0]]
+                off = int(ln.split("offset:")[1])
+                kind = "K" if base < self.vregion else "V"
+                region = 0 if kind == "K" else self.vregion
+                buf = (base + off - region) // self.g.TILE
+                slot = int(args[0].split("[")[1].split(":")[0])
+                self.slots[slot] = self.mem.read((kind, buf))
+            elif op.startswith("v_mfma"):
+                slot = int(args[1].split("[")[1].split(":")[0])
+                j = self.s.get(self.g.S_J, 0) if self.barriers > 1 else -1
+                if args[0].startswith("v["):   # S = K Q^T: K tile j + 1 (the first block: 0)
+                    want = ("K", self.item, j + 1)
+                else:                           # U += V W: V tile j - 1 (the last block: n - 1)
+                    want = ("V", self.item, self.n - 1 if self.fin else j - 1)
+                if self.slots.get(slot) != want:
+                    self.errors.append((ln, self.slots.get(slot), want))
+            if op == "v_add_u32" and "%[nqvo]" in ln:   # the last block sets up the next item's loads
+                self.fin = True
+        return self.errors
+
+
+class _Memory:
+    """LDS buffers of one workgroup: per buffer the loads issued into it, in
+    order; a load is complete once this wavefront waited for it, and visible
+    to every wavefront after the next barrier."""
+
+    def __init__(self):
+        self.vm = []          # VMEM instructions in issue order: (buffer or None, tag)
+        self.done = 0         # VMEM instructions known complete
+        self.visible = 0      # VMEM instructions visible to all wavefronts
+        self.reads_since_barrier = set()
+        self.errors = []
+
+    def vmem(self):
+        self.vm.append((None, None))
+
+    def load(self, buf, tag):
+        if buf in self.reads_since_barrier:
+            self.errors.append(("load into a buffer read since the last barrier", buf, tag))
+        self.vm.append((buf, tag))
+
+    def wait(self, k):
+        self.done = max(self.done, len(self.vm) - k)
+
+    def barrier(self):
+        self.visible = self.done
+        self.reads_since_barrier = set()
+
+    def read(self, buf):
+        self.reads_since_barrier.add(buf)
+        pending = [t for b, t in self.vm[self.visible:] if b == buf]
+        vis = [t for b, t in self.vm[:self.visible] if b == buf]
+        if pending:
+            return ("in flight",) + tuple(pending)
+        return vis[-1] if vis else None
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_lds_buffers_hold_the_tiles_each_product_reads(causal):
+    """Sequences of items of 1 to 9 tiles, in a persistent workgroup's order
+    (the first item loads its own tiles, later ones use their predecessor's
+    prefetch): every MFMA reads the K or V tile that the forward
+    multiplies at that step (S_j = K_j Q^T, then O += V_j P_j), no load targets a buffer read since the last barrier, and no
+    read races a load still in flight."""
+    g = _gen()
+    prog = g.item_asm(causal)
+    for lengths in ([1, 1, 1, 1], [2, 3, 4, 5], [9, 1, 2, 7, 3], [5, 5, 5], [3, 8, 6, 2, 1, 4], [7]):
+        mem = _Memory()
+        for i, n in enumerate(lengths):
+            m = _Machine(g, n, int(i > 0), mem, i)
+            errs = m.run(prog)
+            assert not errs, (lengths, i, errs[:3])
+        assert not mem.errors, (lengths, mem.errors[:3])
+
+
+def test_buffer_checker_catches_planted_mistakes():
+    """The checker is not vacuous: an item that does not wait for its
+    predecessor's prefetch, and a step whose K load goes into the buffer it
+    is reading, are both rejected."""
+    g = _gen()
+    prog = g.item_asm(False)
+    mem = _Memory()
+    assert not _Machine(g, 4, 0, mem, 0).run(prog)
+    bad = [ln.replace(f"vmcnt({g.VM_AFTER_PREFETCH})", "vmcnt(40)") for ln in prog]
+    assert _Machine(g, 3, 1, mem, 1).run(bad) or mem.errors
+    # K_{j+2} into the buffer of K_{j+1}: swap the two K buffers' offsets in
+    # the loop's loads
+    i = next(k for k, ln in enumerate(prog) if ln.startswith("L_loop_"))
+    swapped = prog[:i] + [ln.replace(f"%[wbase], {g.KV_LDS[1]}", "%[wbase], X").replace(
+        f"%[wbase], {g.KV_LDS[0]}", f"%[wbase], {g.KV_LDS[1]}").replace("%[wbase], X", f"%[wbase], {g.KV_LDS[0]}")
+        for ln in prog[i:]]
+    assert swapped != prog
+    mem = _Memory()
+    assert _Machine(g, 6, 0, mem, 0).run(swapped) or mem.errors
 
 
 def test_generator_output_is_deterministic(tmp_path):
