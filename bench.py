@@ -17,9 +17,12 @@ from the fortieth on), so the default W = 60 steps times the steady state.
 Printed: one JSON line.  `value` is fa_fwd TFLOP/s on prefill_8k (algorithmic
 4*B*H*N^2*d FLOPs over the measured kernel time); decode GB/s (algorithmic
 K+V bytes over split+combine time) is reported beside it, together with the
-roofline fractions, the extra workloads (causal_4k, decode_varlen, and the
+roofline fractions against the published peaks and against the ceilings two
+measurement kernels reach in the same run (a bf16 MFMA loop, a read-only HBM
+stream), the extra workloads (fp32_small, causal_4k, decode_varlen, and the
 backward fa_bwd on prefill_8k and causal_4k) and the float64 oracle timed on
-a bounded sample on the host cores.
+a bounded sample on the host cores (which also checks sampled outputs of the
+timed launches).
 """
 
 import argparse
@@ -115,6 +118,22 @@ def cpu_baseline(Q, K, V, seconds, torch):
     }
 
 
+def oracle_fp32_small(Q, K, V):
+    """Host seconds of the oracle on the whole fp32_small workload (the
+    device inputs copied to the host; median of five runs)."""
+    import numpy as np
+
+    import oracle
+
+    q, k, v = (t[0, 0].double().cpu().numpy() for t in (Q, K, V))
+    ts = []
+    for _ in range(5):
+        t0 = time.perf_counter()
+        oracle.attention_rows(q, k, v, 1 / math.sqrt(q.shape[1]), causal=False)
+        ts.append(time.perf_counter() - t0)
+    return float(np.median(ts))
+
+
 def parity_sample(Q, K, V, O, L, q, Kc, Vc, o, lengths, torch):
     import numpy as np
 
@@ -137,6 +156,40 @@ def parity_sample(Q, K, V, O, L, q, Kc, Vc, o, lengths, torch):
         dd = max(dd, float(np.abs(o[0, h].float().cpu().numpy() - o_ref).max()))
     return {"prefill_8k_max_abs_dO": dO, "prefill_8k_max_abs_dL": dL, "decode_32k_max_abs_do": dd,
             "rows_checked": "prefill: 7 rows x 2 heads; decode: 2 heads"}
+
+
+def measured_ceilings(torch, fa, cus):
+    """Ceilings that the two measurement kernels of the library reach on this
+    GPU, timed with HIP events on the stream they run on:
+      * fa_probe_mfma_bf16: 2 workgroups of 4 wavefronts per compute unit,
+        each wavefront 16384 rounds of 4 independent 32x32x16 bf16 MFMAs;
+        also the shader clock its wavefronts ran at (s_memtime cycles over
+        s_memrealtime ticks);
+      * fa_probe_hbm_read: one read of a 4 GiB buffer (16 times the last
+        level cache), 64 workgroups of 256 threads per compute unit."""
+    out = {}
+    wg, iters = 2 * cus, 16384
+    sink = torch.empty(wg * 256, dtype=torch.float32, device="cuda")
+    stamps = torch.zeros(wg, 2, dtype=torch.int64, device="cuda")
+    ms = _timed(lambda i: fa.fa_probe_mfma_bf16(wg, iters, sink, stamps), 5, 3, torch)
+    flop = wg * 4.0 * iters * 4 * 2 * 32 * 32 * 16
+    st = stamps.cpu().double()
+    clk = (st[:, 0] / (st[:, 1] / 1e8)).median().item() / 1e9
+    out["mfma_bf16"] = {"value": round(flop / (ms * 1e-3) / 1e12, 1), "unit": "TFLOP/s",
+                        "kernel": "fa_probe_mfma_bf16", "ms_per_launch": round(ms, 4),
+                        "clock_ghz": round(clk, 3), "workgroups": wg, "iters": iters}
+    del sink, stamps
+    nbytes = 4 << 30
+    buf = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    wg = 64 * cus
+    sink = torch.zeros(wg, dtype=torch.int32, device="cuda")
+    ms = _timed(lambda i: fa.fa_probe_hbm_read(buf, sink), 5, 2, torch)
+    out["hbm_read"] = {"value": round(nbytes / (ms * 1e-3) / 1e9, 1), "unit": "GB/s",
+                       "kernel": "fa_probe_hbm_read", "ms_per_launch": round(ms, 4), "bytes": nbytes,
+                       "workgroups": wg}
+    del buf, sink
+    torch.cuda.synchronize()
+    return out
 
 
 def main():
@@ -280,8 +333,27 @@ def main():
         },
     }
 
-    # ---------------- extra workloads (the causal target and varlen decode)
+    # ---------------- measured ceilings beside the published peaks
+    ceil = measured_ceilings(torch, fa, cus)
+    log(f"ceilings {ceil}")
+    result["roofline"]["measured_ceiling"] = ceil["mfma_bf16"]
+    result["roofline"]["frac_of_measured"] = round(tflops / ceil["mfma_bf16"]["value"], 4)
+    result["decode"]["roofline"]["measured_ceiling"] = ceil["hbm_read"]
+    result["decode"]["roofline"]["frac_of_measured"] = round(dec_gbs / ceil["hbm_read"]["value"], 4)
+
+    # ---------------- extra workloads (the small fp32 case, the causal
+    # target and varlen decode)
     if not args.no_extra:
+        Qs, Ks, Vs = synth.prefill_inputs("fp32_small", dev)
+        Os = torch.empty_like(Qs)
+        Ls = torch.empty(Qs.shape[:3], device=dev)
+        ms_s = _timed(lambda i: fa.fa_fwd_f32(Qs, Ks, Vs, Os, Ls), K_, W_, torch)
+        c1 = synth.WORKLOADS["fp32_small"]
+        fl_s = 4.0 * c1["B"] * c1["H"] * c1["N"] ** 2 * c1["d"]
+        result["fp32_small"] = {"us_per_launch": round(ms_s * 1e3, 2), "unit": "us",
+                                "tflops": round(fl_s / (ms_s * 1e-3) / 1e12, 4),
+                                "shape": "B=1 H=1 N=256 d=64 fp32, non-causal"}
+        log(f"fp32_small {ms_s * 1e3:.2f} us")
         c3 = synth.WORKLOADS["causal_4k"]
         Qc, Kc3, Vc3 = synth.prefill_inputs("causal_4k", dev)
         Oc = torch.empty_like(Qc)
@@ -341,16 +413,19 @@ def main():
             if name != "prefill_8k":
                 del Qb, Kb, Vb
 
-    # ---------------- light parity check of the timed outputs
-    q0, Kc0, Vc0, _ = caches[(K_ - 1) % n_rot]
-    fa.fa_decode(q0, Kc0, Vc0, od, Lkv, num_splits=splits)
-    torch.cuda.synchronize()
-    result["parity_sample"] = parity_sample(
-        Q, K, V, O, L, q0, Kc0.view(Bd, Hd, -1, dd), Vc0.view(Bd, Hd, -1, dd), od, lengths, torch)
-
-    # ---------------- float64 oracle on the host cores
+    # ---------------- float64 oracle on the host cores: the baseline, its
+    # time on fp32_small, and a sampled check of the timed outputs
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(Q, K, V, args.cpu_seconds, torch)
+        cb = cpu_baseline(Q, K, V, args.cpu_seconds, torch)
+        if "fp32_small" in result:
+            cb["fp32_small_seconds"] = round(oracle_fp32_small(Qs, Ks, Vs), 5)
+            result["fp32_small"]["oracle_seconds"] = cb["fp32_small_seconds"]
+        q0, Kc0, Vc0, _ = caches[(K_ - 1) % n_rot]
+        fa.fa_decode(q0, Kc0, Vc0, od, Lkv, num_splits=splits)
+        torch.cuda.synchronize()
+        cb["check"] = parity_sample(
+            Q, K, V, O, L, q0, Kc0.view(Bd, Hd, -1, dd), Vc0.view(Bd, Hd, -1, dd), od, lengths, torch)
+        result["cpu_baseline"] = cb
         log(f"cpu baseline {result['cpu_baseline']}")
 
     print(json.dumps(result), flush=True)

@@ -30,6 +30,8 @@ from ._binding import (  # noqa: F401
     fa_fwd,
     fa_fwd_f32,
     fa_fwd_plan,
+    fa_probe_hbm_read,
+    fa_probe_mfma_bf16,
     fa_release_workspace,
     last_error,
     lib,

@@ -12,7 +12,9 @@ import math
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libfa.so")
+# FA_LIBRARY names another build of the same sources (the host-sanitizer
+# build of the dispatch code, for instance); the default is the in-tree one.
+LIB_PATH = os.environ.get("FA_LIBRARY") or os.path.join(_HERE, "libfa.so")
 
 FA_OK = 0
 FA_ERR_INVALID_ARG = -1
@@ -77,6 +79,8 @@ def _load():
         "fa_decode_plan": (I, [I, I, I, I, ctypes.POINTER(fa_decode_plan_t)]),
         "fa_decode_chunk_tokens": (I, [I, I]),
         "fa_release_workspace": (I, []),
+        "fa_probe_hbm_read": (I, [P, Z, I, P, P]),
+        "fa_probe_mfma_bf16": (I, [I, I, P, P, P]),
         "fa_status_string": (ctypes.c_char_p, [I]),
         "fa_last_error": (ctypes.c_char_p, []),
         "fa_version": (I, []),
@@ -107,6 +111,8 @@ EXPORTED = (
     "fa_decode_plan",
     "fa_decode_chunk_tokens",
     "fa_release_workspace",
+    "fa_probe_hbm_read",
+    "fa_probe_mfma_bf16",
     "fa_status_string",
     "fa_last_error",
     "fa_version",
@@ -337,3 +343,33 @@ def fa_decode_paged(q, Kpool, Vpool, o, block_table, Lkv, lse_out=None, num_spli
                                int(block_size), d, int(num_splits), float(scale), _ptr(workspace), nbytes,
                                _stream_ptr(stream)))
     return o, lse_out
+
+
+# --------------------------------------------------------------------------
+# measurement kernels (measured ceilings beside the published peaks)
+# --------------------------------------------------------------------------
+
+def fa_probe_hbm_read(buf, sink, workgroups=None, stream=None):
+    """Reads every byte of the contiguous device tensor `buf` once; sink is a
+    uint32/int32 device tensor of at least `workgroups` elements (default:
+    its length)."""
+    if workgroups is None:
+        workgroups = sink.numel()
+    if sink.numel() * sink.element_size() < 4 * workgroups or sink.element_size() != 4:
+        raise ValueError("sink must hold one 4-byte word per workgroup")
+    for t, n in ((buf, "buf"), (sink, "sink")):
+        if not t.is_contiguous() or t.device.type != "cuda":
+            raise ValueError(f"{n} must be a contiguous device tensor")
+    _check(lib.fa_probe_hbm_read(_ptr(buf), buf.numel() * buf.element_size(), int(workgroups), _ptr(sink),
+                                 _stream_ptr(stream)))
+
+
+def fa_probe_mfma_bf16(workgroups, iters, sink, stamps=None, stream=None):
+    """workgroups x 4 wavefronts of iters x 4 bf16 MFMAs (32x32x16); sink
+    float32 [workgroups * 256], stamps int64 [workgroups, 2] or None."""
+    import torch
+
+    _expect(sink, torch.float32, (workgroups * 256,), "sink")
+    if stamps is not None:
+        _expect(stamps, torch.int64, (workgroups, 2), "stamps")
+    _check(lib.fa_probe_mfma_bf16(int(workgroups), int(iters), _ptr(sink), _ptr(stamps), _stream_ptr(stream)))

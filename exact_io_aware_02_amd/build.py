@@ -1,6 +1,6 @@
 """Build libfa.so (the HIP kernels and the C ABI) in-tree for gfx950.
 
-    python exact_io_aware_02_amd/build.py [--verbose] [--resource-usage]
+    python exact_io_aware_02_amd/build.py [--verbose] [--resource-usage] [--host-sanitizers]
 
 (run as a script: importing the package would load the library first)
 
@@ -22,7 +22,7 @@ OBJDIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libfa.so")
 
 SOURCES = ["fa_api.hip", "fa_fwd_bf16.hip", "fa_fwd_bf16_asm.hip", "fa_fwd_f32.hip", "fa_decode.hip",
-           "fa_bwd_bf16.hip"]
+           "fa_bwd_bf16.hip", "fa_probe.hip"]
 # generated before compiling: the assembly of the 64-rows-per-wavefront
 # forward's tile loop (fa_fwd_bf16_asm.hip includes it)
 GENERATED = os.path.join(CSRC, "fa_fwd_asm_d128.inc")
@@ -92,6 +92,41 @@ def build(verbose=False, resource_usage=False):
     return LIB
 
 
+SAN_DIR = os.path.join(OBJDIR, "host_sanitizers")
+SAN_LIB = os.path.join(SAN_DIR, "libfa_san.so")
+# AddressSanitizer and UndefinedBehaviorSanitizer on the host pass only (the
+# device code of the same file is compiled as usual)
+SAN_FLAGS = ["-Xarch_host", "-g", "-Xarch_host", "-fno-omit-frame-pointer",
+             "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-sanitize-recover=all"]
+
+
+def build_host_sanitized(verbose=False):
+    """libfa_san.so: the host dispatch (fa_api.hip: argument checks, overlap
+    tests, planners, the workspace and scratch maps) compiled with ASan and
+    UBSan, linked with the objects of the ordinary build (built first if
+    missing).  Load it with the ASan runtime preloaded (asan_runtime())."""
+    hipcc = _hipcc()
+    objs = [os.path.join(OBJDIR, src.replace(".hip", ".o")) for src in SOURCES if src != "fa_api.hip"]
+    if not all(os.path.exists(o) for o in objs):
+        build(verbose)
+    os.makedirs(SAN_DIR, exist_ok=True)
+    api = os.path.join(SAN_DIR, "fa_api.o")
+    _run([hipcc, *FLAGS, *SAN_FLAGS, "-c", os.path.join(CSRC, "fa_api.hip"), "-o", api], verbose)
+    tmp = SAN_LIB + ".tmp"
+    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Xarch_host", "-fsanitize=address",
+          "-Xarch_host", "-fsanitize=undefined", "-shared-libsan", api, *objs, "-o", tmp], verbose)
+    os.replace(tmp, SAN_LIB)
+    return SAN_LIB
+
+
+def asan_runtime():
+    """Path of the compiler's shared ASan runtime (to preload into Python)."""
+    p = subprocess.run([_hipcc(), "-print-file-name=libclang_rt.asan-x86_64.so"], stdout=subprocess.PIPE,
+                       stderr=subprocess.DEVNULL, text=True).stdout.strip()
+    return p if p and os.path.isabs(p) and os.path.exists(p) else None
+
+
 def _check_undefined(path):
     """Fail if the host pass dropped a kernel launch stub (the library would
     then not load)."""
@@ -108,6 +143,10 @@ if __name__ == "__main__":
     ap = argparse.ArgumentParser()
     ap.add_argument("--verbose", action="store_true")
     ap.add_argument("--resource-usage", action="store_true", help="print VGPR/LDS usage per kernel")
+    ap.add_argument("--host-sanitizers", action="store_true",
+                    help="also build libfa_san.so (host dispatch with ASan + UBSan)")
     a = ap.parse_args()
     print(build(verbose=a.verbose, resource_usage=a.resource_usage))
+    if a.host_sanitizers:
+        print(build_host_sanitized(verbose=a.verbose))
     sys.exit(0)

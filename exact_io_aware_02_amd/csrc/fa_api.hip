@@ -544,6 +544,30 @@ int fa_decode_paged_splits(int B, int H, int max_blocks, int block_size, int num
   return fa::paged_blocks_per_chunk(fa::decode_chunk_tokens((int)max_len, S), block_size) <= fa::kPagedIdsPerChunk ? S : 0;
 }
 
+int fa_probe_hbm_read(const void* buf, size_t bytes, int workgroups, uint32_t* sink, void* stream) {
+  if (!buf || !sink) return fail(FA_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned(buf, 16) || !aligned(sink, 4)) return fail(FA_ERR_INVALID_ARG, "buf must be 16-byte and sink 4-byte aligned");
+  if (bytes == 0 || bytes % 16) return fail(FA_ERR_INVALID_ARG, "bytes must be a positive multiple of 16 (got %zu)", bytes);
+  if (workgroups < 1 || workgroups > (1 << 20))
+    return fail(FA_ERR_INVALID_ARG, "workgroups must be in [1, 1048576] (got %d)", workgroups);
+  if (overlap(buf, bytes, sink, (size_t)workgroups * 4)) return fail(FA_ERR_INVALID_ARG, "sink overlaps buf");
+  hipError_t e = fa::launch_probe_hbm_read(buf, bytes, workgroups, sink, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ok() : hip_fail(e, "probe launch");
+}
+
+int fa_probe_mfma_bf16(int workgroups, int iters, float* sink, uint64_t* stamps, void* stream) {
+  if (!sink) return fail(FA_ERR_INVALID_ARG, "null sink");
+  if (!aligned(sink, 4) || (stamps && !aligned(stamps, 8)))
+    return fail(FA_ERR_INVALID_ARG, "sink must be 4-byte and stamps 8-byte aligned");
+  if (workgroups < 1 || workgroups > (1 << 20))
+    return fail(FA_ERR_INVALID_ARG, "workgroups must be in [1, 1048576] (got %d)", workgroups);
+  if (iters < 1 || iters > (1 << 24)) return fail(FA_ERR_INVALID_ARG, "iters must be in [1, 16777216] (got %d)", iters);
+  if (stamps && overlap(sink, (size_t)workgroups * 256 * 4, stamps, (size_t)workgroups * 16))
+    return fail(FA_ERR_INVALID_ARG, "stamps overlaps sink");
+  hipError_t e = fa::launch_probe_mfma_bf16(workgroups, iters, sink, stamps, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ok() : hip_fail(e, "probe launch");
+}
+
 int fa_release_workspace(void) {
   std::lock_guard<std::mutex> lk(g_ws_mu);
   int prev = 0;

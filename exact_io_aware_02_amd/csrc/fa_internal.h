@@ -113,6 +113,9 @@ hipError_t launch_fwd_bf16_asm(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdArgs& a, int d, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, int d, hipStream_t stream);
 hipError_t launch_bwd_bf16(const BwdArgs& a, int d, hipStream_t stream);
+hipError_t launch_probe_hbm_read(const void* buf, size_t bytes, int workgroups, uint32_t* sink,
+                                 hipStream_t stream);
+hipError_t launch_probe_mfma_bf16(int workgroups, int iters, float* sink, uint64_t* stamps, hipStream_t stream);
 
 // Host-side tile bookkeeping used by both the planner and the launcher.
 __host__ __device__ inline int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }

@@ -265,6 +265,33 @@ int fa_decode_chunk_tokens(int kv_len, int num_splits);
  * (synchronises the devices that own them).  Returns FA_OK or FA_ERR_HIP. */
 int fa_release_workspace(void);
 
+/* Measurement kernels (no attention): the measured ceilings that a roofline
+ * places next to the published peaks ("CMU 10-423 Lecture 18", section 6,
+ * the roofline model).
+ *
+ * fa_probe_hbm_read: reads every 16-byte word of buf once (workgroups of 256
+ * threads striding over the buffer, eight loads in flight per thread) and
+ * writes nothing but, with negligible probability, one word of sink.
+ *   buf   : device, 16-byte aligned, `bytes` readable bytes
+ *   bytes : > 0, a multiple of 16
+ *   workgroups : in [1, 1048576]
+ *   sink  : device uint32 [workgroups], 4-byte aligned, not overlapping buf
+ * Algorithmic traffic: `bytes` read per launch.
+ *
+ * fa_probe_mfma_bf16: every wavefront of `workgroups` x 4 runs `iters` rounds
+ * of four independent v_mfma_f32_32x32x16_bf16 (32768 FLOP each), i.e.
+ * workgroups * 4 * iters * 4 * 32768 FLOP per launch.
+ *   workgroups : in [1, 1048576]; iters : in [1, 16777216]
+ *   sink  : device float [workgroups * 256], 4-byte aligned (one value per
+ *           thread, so the products cannot be dropped)
+ *   stamps: device uint64 [2 * workgroups], 8-byte aligned, or NULL; for
+ *           each workgroup, the shader-clock cycles and the 100 MHz
+ *           constant-clock ticks its first wavefront spent in the loop
+ *           (cycles / (ticks / 1e8) = the clock it ran at)
+ * Both: errors FA_ERR_INVALID_ARG (checked before any HIP call), FA_ERR_HIP. */
+int fa_probe_hbm_read(const void* buf, size_t bytes, int workgroups, uint32_t* sink, void* stream);
+int fa_probe_mfma_bf16(int workgroups, int iters, float* sink, uint64_t* stamps, void* stream);
+
 /* Static description of a status code, and the thread-local message of the
  * last failing call on this thread ("" if none). */
 const char* fa_status_string(int status);

@@ -321,3 +321,20 @@ def test_bwd_workspace_formula():
     for B, H, N in ((1, 1, 1), (2, 3, 100), (1, 32, 8192)):
         assert fa.fa_bwd_workspace_bytes(B, H, N) == -(-(B * H * N * 4) // 256) * 256
     assert fa.fa_bwd_workspace_bytes(0, 1, 1) == 0
+
+
+def test_probes_reject_invalid_arguments():
+    """The measurement kernels check their buffers and sizes on the host."""
+    fa = _fa()
+    lib = fa.lib
+    assert lib.fa_probe_hbm_read(None, 1024, 4, A, None) == -1
+    assert lib.fa_probe_hbm_read(A, 1000, 4, 2 * A, None) == -1          # not a multiple of 16
+    assert lib.fa_probe_hbm_read(A + 8, 1024, 4, 2 * A, None) == -1      # misaligned
+    assert lib.fa_probe_hbm_read(A, 1024, 0, 2 * A, None) == -1
+    assert lib.fa_probe_hbm_read(A, 1024, 4, A + 512, None) == -1        # sink inside buf
+    assert "overlaps" in fa.last_error()
+    assert lib.fa_probe_mfma_bf16(4, 10, None, None, None) == -1
+    assert lib.fa_probe_mfma_bf16(0, 10, A, None, None) == -1
+    assert lib.fa_probe_mfma_bf16(4, 0, A, None, None) == -1
+    assert lib.fa_probe_mfma_bf16(4, 10, A, A + 4, None) == -1           # stamps misaligned
+    assert lib.fa_probe_mfma_bf16(4, 10, A, A + 8, None) == -1           # stamps inside sink
