@@ -393,9 +393,11 @@ int fa_decode(const void* q, const void* Kcache, const void* Vcache, void* o, in
   return decode_common(q, Kcache, Vcache, o, nullptr, B, H, Lkv, 0, d, S, scale, ws, hs);
 }
 
+// The backward's workspace: D, then L in base 2, each B * H * N floats
+// aligned to 256 bytes.
 size_t fa_bwd_workspace_bytes(int B, int H, int N) {
   if (B < 1 || H < 1 || N < 1) return 0;
-  return align256((size_t)B * H * N * sizeof(float));
+  return 2 * align256((size_t)B * H * N * sizeof(float));
 }
 
 int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* L, void* dQ,
@@ -419,7 +421,9 @@ int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const voi
       if (overlap(workspace, need, p, tb)) return fail(FA_ERR_INVALID_ARG, "workspace overlaps a tensor");
     if (overlap(workspace, need, L, lb)) return fail(FA_ERR_INVALID_ARG, "workspace overlaps L");
   }
-  fa::BwdArgs a{Q, K, V, O, dO, L, dQ, dK, dV, static_cast<float*>(ws), B, H, N, causal, scale};
+  float* Dws = static_cast<float*>(ws);
+  float* L2ws = reinterpret_cast<float*>(static_cast<char*>(ws) + need / 2);
+  fa::BwdArgs a{Q, K, V, O, dO, L, dQ, dK, dV, Dws, L2ws, B, H, N, causal, scale};
   hipError_t e = fa::launch_bwd_bf16(a, d, hs);
   if (e != hipSuccess) return hip_fail(e, "fa_bwd launch");
   return ok();

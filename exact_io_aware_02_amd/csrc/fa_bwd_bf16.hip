@@ -11,7 +11,9 @@
 // with P, dP and dS recomputed tile by tile and never stored.
 //
 // Three launches, no atomics (so results do not depend on timing):
-//  1. bwd_dot_kernel: D for every row (HBM-bound, 2 N d bf16 reads per head).
+//  1. bwd_dot_kernel: D for every row, and L in base 2 (L log2 e) so that
+//     P = exp2(S scale log2 e - L log2 e) is one fma and one exp2 per element
+//     (HBM-bound, 2 N d bf16 reads per head).
 //  2. bwd_dkdv_kernel: a workgroup owns kBwdKV keys (32 per wavefront, K and
 //     V held in registers as MFMA B operands) and walks query tiles of
 //     kBwdQT rows staged in LDS with their L and D: S, P, dV^T += dO^T P,
@@ -111,7 +113,8 @@ __device__ __forceinline__ void store_rows(__bf16* base, int row, int N, const f
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void bwd_dot_kernel(const __bf16* __restrict__ O, const __bf16* __restrict__ dO,
-                                                      float* __restrict__ Dout, long long rows) {
+                                                      const float* __restrict__ L, float* __restrict__ Dout,
+                                                      float* __restrict__ L2out, long long rows) {
   constexpr int LPR = D / 8;       // lanes per row (16 bytes each)
   constexpr int RPW = 64 / LPR;    // rows per wavefront
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -128,7 +131,10 @@ __global__ __launch_bounds__(256) void bwd_dot_kernel(const __bf16* __restrict__
   }
 #pragma unroll
   for (int off = 1; off < LPR; off <<= 1) acc += __shfl_xor(acc, off);
-  if (row < rows && lane % LPR == 0) Dout[row] = acc;
+  if (row < rows && lane % LPR == 0) {
+    Dout[row] = acc;
+    L2out[row] = L[row] * kLog2e;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -137,7 +143,7 @@ __global__ __launch_bounds__(256) void bwd_dot_kernel(const __bf16* __restrict__
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dkdv_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ Kg, const __bf16* __restrict__ Vg,
-                     const __bf16* __restrict__ dOg, const float* __restrict__ Lg, const float* __restrict__ Dg,
+                     const __bf16* __restrict__ dOg, const float* __restrict__ L2g, const float* __restrict__ Dg,
                      __bf16* __restrict__ dKg, __bf16* __restrict__ dVg, int N, int kv_tiles, float scale) {
   using T = BwdTile<D>;
   // per buffer s: [Q tile][dO tile][L][D]
@@ -181,7 +187,7 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ K
   const int qt0 = CAUSAL ? (kt * kBwdKV) / kBwdQT : 0;
   const u32x4_t q_rsrc = make_rsrc(Qg + head, head_bytes);
   const u32x4_t do_rsrc = make_rsrc(dOg + head, head_bytes);
-  const u32x4_t l_rsrc = make_rsrc(Lg + (size_t)bh * N, (unsigned)N * 4);
+  const u32x4_t l_rsrc = make_rsrc(L2g + (size_t)bh * N, (unsigned)N * 4);
   const u32x4_t d_rsrc = make_rsrc(Dg + (size_t)bh * N, (unsigned)N * 4);
   auto issue = [&](int t, int s) {
     const unsigned soff = (unsigned)t * kBwdQT * T::kRowBytes;
@@ -211,6 +217,9 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ K
     const char LDS_AS* qtile = qbuf(s);
     const char LDS_AS* otile = dobuf(s);
     const int q0 = t * kBwdQT;
+    // every (query, key) pair of this wavefront's tile is valid: no per-element
+    // masks (all tiles but a ragged last one and, causal, the diagonal ones)
+    const bool full = q0 + kBwdQT <= N && (!CAUSAL || kt * kBwdKV + wave * 32 + 31 <= q0);
 
     // S = Q K^T (query rows, the lane's key in the column), 2 blocks of 32 queries
     f32x16_t sc[kBwdQT / 32], dp[kBwdQT / 32];
@@ -224,26 +233,40 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ K
         sc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kf[ds], sc[qb], 0, 0, 0);
       }
     }
-    // P = exp(S - L_row); rows past N and (causal) queries before the key get 0.
-    // Element i of block qb is query q0 + 32 qb + 8 (i >> 2) + 4 g + (i & 3).
+    // P = exp2(S c - L_row log2 e) (L staged in base 2); rows past N and
+    // (causal) queries before the key get 0.  Element i of block qb is query
+    // q0 + 32 qb + 8 (i >> 2) + 4 g + (i & 3).
     bf16x8_t pb[kBwdQT / 16];
     float pf[kBwdQT / 32][16];
+    if (full) {
 #pragma unroll
-    for (int qb = 0; qb < kBwdQT / 32; ++qb) {
+      for (int qb = 0; qb < kBwdQT / 32; ++qb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int rl = 32 * qb + 8 * r + 4 * g;  // first of 4 consecutive local rows
-        const f32x4_t L4 = *(const f32x4_t LDS_AS*)(lbuf(s) + rl);
+        for (int r = 0; r < 4; ++r) {
+          const f32x4_t L4 = *(const f32x4_t LDS_AS*)(lbuf(s) + 32 * qb + 8 * r + 4 * g);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int qrow = q0 + rl + e;
-          const bool ok = qrow < N && (!CAUSAL || key <= qrow);
-          pf[qb][4 * r + e] = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(sc[qb][4 * r + e], c, -L4[e] * kLog2e)) : 0.f;
+          for (int e = 0; e < 4; ++e)
+            pf[qb][4 * r + e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[qb][4 * r + e], c, -L4[e]));
         }
-      }
+    } else {
+#pragma unroll
+      for (int qb = 0; qb < kBwdQT / 32; ++qb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int rl = 32 * qb + 8 * r + 4 * g;  // first of 4 consecutive local rows
+          const f32x4_t L4 = *(const f32x4_t LDS_AS*)(lbuf(s) + rl);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int qrow = q0 + rl + e;
+            const bool ok = qrow < N && (!CAUSAL || key <= qrow);
+            pf[qb][4 * r + e] = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(sc[qb][4 * r + e], c, -L4[e])) : 0.f;
+          }
+        }
+    }
+#pragma unroll
+    for (int qb = 0; qb < kBwdQT / 32; ++qb)
 #pragma unroll
       for (int h = 0; h < 2; ++h) pb[2 * qb + h] = to_bf16x8(&pf[qb][8 * h]);
-    }
     // dV^T += dO^T P (queries are the contraction index)
 #pragma unroll
     for (int ks = 0; ks < kBwdQT / 16; ++ks) {
@@ -366,6 +389,8 @@ void bwd_dq_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ Kg,
     const char LDS_AS* kb = kbuf(s);
     const char LDS_AS* vb = vbuf(s);
     const int k0 = j * kBwdKT;
+    // every (query, key) pair of this wavefront's tile is valid: no per-element masks
+    const bool full = k0 + kBwdKT <= N && qw0 + 32 <= N && (!CAUSAL || k0 + kBwdKT - 1 <= qw0);
 
     // S^T = K Q^T and dP^T = V dO^T (key rows, the lane's query in the column)
     f32x16_t sc[kKB], dp[kKB];
@@ -391,19 +416,28 @@ void bwd_dq_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ Kg,
     // keys after the query get 0.  Element i of block cb is key
     // k0 + 32 cb + 8 (i >> 2) + 4 g + (i & 3).
     bf16x8_t dsb[kBwdKT / 16];
+    float dsf[kKB][16];
+    if (full) {
 #pragma unroll
-    for (int cb = 0; cb < kKB; ++cb) {
-      float dsf[16];
+      for (int cb = 0; cb < kKB; ++cb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int kr = k0 + 32 * cb + 8 * (i >> 2) + 4 * g + (i & 3);
-        const bool ok = kr < N && qrow < N && (!CAUSAL || kr <= qrow);
-        const float p = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(sc[cb][i], c, -L2)) : 0.f;
-        dsf[i] = p * (dp[cb][i] - Dq);
-      }
+        for (int i = 0; i < 16; ++i)
+          dsf[cb][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[cb][i], c, -L2)) * (dp[cb][i] - Dq);
+    } else {
 #pragma unroll
-      for (int h = 0; h < 2; ++h) dsb[2 * cb + h] = to_bf16x8(&dsf[8 * h]);
+      for (int cb = 0; cb < kKB; ++cb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int kr = k0 + 32 * cb + 8 * (i >> 2) + 4 * g + (i & 3);
+          const bool ok = kr < N && qrow < N && (!CAUSAL || kr <= qrow);
+          const float p = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(sc[cb][i], c, -L2)) : 0.f;
+          dsf[cb][i] = p * (dp[cb][i] - Dq);
+        }
     }
+#pragma unroll
+    for (int cb = 0; cb < kKB; ++cb)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) dsb[2 * cb + h] = to_bf16x8(&dsf[cb][8 * h]);
     // dQ^T += K^T dS^T (keys are the contraction index)
 #pragma unroll
     for (int ks = 0; ks < kBwdKT / 16; ++ks) {
@@ -422,15 +456,15 @@ hipError_t launch(const BwdArgs& a, hipStream_t stream) {
   const long long rows = (long long)a.B * a.H * a.N;
   constexpr int kRowsPerDotBlock = 4 * (64 / (D / 8));
   hipLaunchKernelGGL((bwd_dot_kernel<D>), dim3((unsigned)((rows + kRowsPerDotBlock - 1) / kRowsPerDotBlock)),
-                     dim3(256), 0, stream, static_cast<const __bf16*>(a.O), static_cast<const __bf16*>(a.dO),
-                     a.Dws, rows);
+                     dim3(256), 0, stream, static_cast<const __bf16*>(a.O), static_cast<const __bf16*>(a.dO), a.L,
+                     a.Dws, a.L2ws, rows);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int bh = a.B * a.H;
   const int kv_tiles = (a.N + kBwdKV - 1) / kBwdKV;
   hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)(bh * kv_tiles)), dim3(kThreads), 0, stream,
                      static_cast<const __bf16*>(a.Q), static_cast<const __bf16*>(a.K),
-                     static_cast<const __bf16*>(a.V), static_cast<const __bf16*>(a.dO), a.L, a.Dws,
+                     static_cast<const __bf16*>(a.V), static_cast<const __bf16*>(a.dO), a.L2ws, a.Dws,
                      static_cast<__bf16*>(a.dK), static_cast<__bf16*>(a.dV), a.N, kv_tiles, a.scale);
   e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -77,7 +77,8 @@ struct BwdArgs {
   void* dQ;
   void* dK;
   void* dV;
-  float* Dws;  // [B, H, N] fp32 workspace: D_i = dO_i . O_i
+  float* Dws;   // [B, H, N] fp32 workspace: D_i = dO_i . O_i
+  float* L2ws;  // [B, H, N] fp32 workspace: L_i log2 e
   int B, H, N;
   int causal;
   float scale;

@@ -121,7 +121,7 @@ int fa_fwd_f32(const float* Q, const float* K, const float* V, float* O, float* 
  *             nearest-even from fp32
  *   causal, scale : as in fa_fwd
  *   workspace : device memory of at least fa_bwd_workspace_bytes(B, H, N)
- *             bytes, 256-byte aligned, for D; or NULL with workspace_bytes = 0
+ *             bytes, 256-byte aligned, for D and L log2 e; or NULL with workspace_bytes = 0
  *             to use the library's workspace of the (device, stream) (grown
  *             with hipMalloc, so not while the stream is being captured)
  * Arithmetic: bf16 MFMA products with fp32 accumulation; P and dS are rounded
@@ -135,8 +135,8 @@ int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const voi
            void* dQ, void* dK, void* dV, int B, int H, int N, int d, int causal, float scale,
            void* workspace, size_t workspace_bytes, void* stream);
 
-/* Workspace bytes fa_bwd needs (B * H * N floats, rounded up to 256);
- * 0 for invalid arguments. */
+/* Workspace bytes fa_bwd needs (two arrays of B * H * N floats, each
+ * rounded up to 256 bytes); 0 for invalid arguments. */
 size_t fa_bwd_workspace_bytes(int B, int H, int N);
 
 /*

@@ -319,7 +319,7 @@ def test_bwd_rejects_invalid_arguments(kw, status, msg):
 def test_bwd_workspace_formula():
     fa = _fa()
     for B, H, N in ((1, 1, 1), (2, 3, 100), (1, 32, 8192)):
-        assert fa.fa_bwd_workspace_bytes(B, H, N) == -(-(B * H * N * 4) // 256) * 256
+        assert fa.fa_bwd_workspace_bytes(B, H, N) == 2 * (-(-(B * H * N * 4) // 256) * 256)
     assert fa.fa_bwd_workspace_bytes(0, 1, 1) == 0
 
 
