@@ -279,10 +279,15 @@ class _Machine:
     wavefronts run the same program, so a load is visible to every wavefront
     at the first barrier after this wavefront has waited for it."""
 
-    def __init__(self, g, n, pre, mem, item):
+    def __init__(self, g, n, pre, mem, item, wave=0, exec0_counts=True):
         self.g, self.n, self.mem, self.item = g, n, mem, item
+        # the last 1 KiB block of a tile is loaded by wavefront 0 only; the
+        # others issue that load with EXEC = 0, which may or may not count in
+        # vmcnt (both are checked)
+        self.exec_on = True
+        self.exec0_counts = exec0_counts
         self.vregion = g.KV_LDS[2]          # V buffers follow the K buffers
-        self.ops = {"%[n]": n, "%[pre]": pre, "%[wbase]": 0, "%[wave]": 0,
+        self.ops = {"%[n]": n, "%[pre]": pre, "%[wbase]": 0, "%[wave]": wave,
                     "%[kb]": 0, "%[vb]": self.vregion, "%[hb]": n * 16384, "%[nhb]": 1 << 24,
                     "%[klo]": 0, "%[vlo]": 0, "%[nklo]": 1 << 28, "%[nvlo]": 1 << 28, "%[khi]": 0, "%[vhi]": 0,
                     "%[nkhi]": 0, "%[nvhi]": 0, "%[n_keys]": 64 * n, "%[qw0]": 0, "%[c]": 0, "%[theta]": 0}
@@ -339,6 +344,10 @@ class _Machine:
             elif op.startswith("s_cmp_"):
                 a_, b_ = self.val(args[0]), self.val(args[1])
                 scc = int({"eq": a_ == b_, "lg": a_ != b_, "lt": a_ < b_, "gt": a_ > b_, "ge": a_ >= b_}[op[6:8]])
+            elif op == "s_cselect_b64" and args[0] == "exec":
+                self.exec_on = bool(scc)
+            elif op == "s_mov_b64" and args[0] == "exec":
+                self.exec_on = True
             elif op == "s_cbranch_scc1":
                 if scc:
                     pc = labels[args[0]]
@@ -364,7 +373,10 @@ class _Machine:
                 region = 0 if kind == "K" else self.vregion
                 buf = (self.m0 - region) // self.g.TILE
                 assert self.m0 % 1024 == 0 and 0 <= buf < 3, (ln, self.m0)
-                self.mem.load((kind, buf), (kind, item, tile))
+                if self.exec_on:
+                    self.mem.load((kind, buf), (kind, item, tile))
+                elif self.exec0_counts:
+                    self.mem.vmem()
             elif op.startswith("buffer_load") or op.startswith("buffer_store"):
                 self.mem.vmem()
             elif op.startswith("ds_read") and ("%[kb]" in ln or "%[vb]" in ln):
@@ -375,6 +387,8 @@ class _Machine:
                 buf = (base + off - region) // self.g.TILE
                 slot = int(args[0].split("[")[1].split(":")[0])
                 self.slots[slot] = self.mem.read((kind, buf))
+            elif op == "v_add_u32" and "%[nqvo]" in ln:   # the final block sets up the next item's loads
+                self.fin = True
             elif op.startswith("v_mfma"):
                 slot = int(args[1].split("[")[1].split(":")[0])
                 j = self.s.get(self.g.S_J, 0) if self.barriers > 1 else -1
@@ -384,8 +398,6 @@ class _Machine:
                     want = ("V", self.item, self.n - 1 if self.fin else j - 1)
                 if self.slots.get(slot) != want:
                     self.errors.append((ln, self.slots.get(slot), want))
-            if op == "v_add_u32" and "%[nqvo]" in ln:   # the last block sets up the next item's loads
-                self.fin = True
         return self.errors
 
 
@@ -425,8 +437,9 @@ class _Memory:
         return vis[-1] if vis else None
 
 
+@pytest.mark.parametrize("wave,exec0_counts", [(0, True), (1, True), (1, False)])
 @pytest.mark.parametrize("causal", [False, True])
-def test_lds_buffers_hold_the_tiles_each_product_reads(causal):
+def test_lds_buffers_hold_the_tiles_each_product_reads(causal, wave, exec0_counts):
     """Sequences of items of 1 to 9 tiles, in a persistent workgroup's order
     (the first item loads its own tiles, later ones use their predecessor's
     prefetch): every MFMA reads the K or V tile that the forward
@@ -437,7 +450,7 @@ def test_lds_buffers_hold_the_tiles_each_product_reads(causal):
     for lengths in ([1, 1, 1, 1], [2, 3, 4, 5], [9, 1, 2, 7, 3], [5, 5, 5], [3, 8, 6, 2, 1, 4], [7]):
         mem = _Memory()
         for i, n in enumerate(lengths):
-            m = _Machine(g, n, int(i > 0), mem, i)
+            m = _Machine(g, n, int(i > 0), mem, i, wave, exec0_counts)
             errs = m.run(prog)
             assert not errs, (lengths, i, errs[:3])
         assert not mem.errors, (lengths, mem.errors[:3])
