@@ -97,7 +97,7 @@ def test_fp32_worked_example_49_over_15():
 
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("N", [1, 63, 65, 200])
+@pytest.mark.parametrize("N", [1, 63, 65, 200, 700])
 def test_fp32_small_shapes(N, d, causal):
     fa = _fa()
     _say("fp32", N, d, causal)
