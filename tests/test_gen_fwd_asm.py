@@ -392,8 +392,11 @@ class _Machine:
             elif op.startswith("v_mfma"):
                 slot = int(args[1].split("[")[1].split(":")[0])
                 j = self.s.get(self.g.S_J, 0) if self.barriers > 1 else -1
-                if args[0].startswith("v["):   # S = K Q^T: K tile j + 1 (the first block: 0)
-                    want = ("K", self.item, j + 1)
+                if args[0].startswith("v["):   # S_t = K_t Q^T into S buffer t & 1
+                    # step j forms S_{j+1}, or completes S_j with the
+                    # products its predecessor deferred (the first block: S_0)
+                    par = 0 if int(args[0][2:].split(":")[0]) < self.g.S_BUF[1] else 1
+                    want = ("K", self.item, j + 1 if par == (j + 1) % 2 else j)
                 else:                           # U += V W: V tile j - 1 (the last block: n - 1)
                     want = ("V", self.item, self.n - 1 if self.fin else j - 1)
                 if self.slots.get(slot) != want:
