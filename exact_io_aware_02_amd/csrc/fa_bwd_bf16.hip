@@ -108,6 +108,16 @@ __device__ __forceinline__ void store_rows(__bf16* base, int row, int N, const f
   }
 }
 
+// Logical index of workgroup b of G such that the workgroups placed on one
+// XCD (the dispatcher deals workgroups round-robin over the 8 XCDs) get
+// consecutive logical indices, so one head's items run on one XCD and share
+// its L2.  A bijection on [0, G) whatever the actual placement.
+__device__ __forceinline__ int xcd_local_index(int b, int G) {
+  const int per = G >> 3, rem = G & 7;
+  const int xcd = b & 7, slot = b >> 3;
+  return xcd * per + (xcd < rem ? xcd : rem) + slot;
+}
+
 // ---------------------------------------------------------------------------
 // 1. D_i = G_i . O_i
 // ---------------------------------------------------------------------------
@@ -157,11 +167,12 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ K
   auto lbuf = [&](int s) { return (const float LDS_AS*)(lds + s * kBuf + 2 * T::kQTBytes); };
   auto dbuf = [&](int s) { return (const float LDS_AS*)(lds + s * kBuf + 2 * T::kQTBytes + T::kStatBytes); };
 
-  // work item: key tile kt of head bh; tiles are numbered key-tile major so
-  // the longest causal items (first key tiles) start first
-  const int bh_count = gridDim.x / kv_tiles;
-  const int kt = blockIdx.x / bh_count;
-  const int bh = blockIdx.x - kt * bh_count;
+  // work item: key tile kt of head bh, head-major over XCD-local logical
+  // indices (a head's Q and dO tiles are re-read by all its key tiles, from
+  // one L2); within a head the longest causal items (first key tiles) first
+  const int lw = xcd_local_index(blockIdx.x, gridDim.x);
+  const int bh = lw / kv_tiles;
+  const int kt = lw - bh * kv_tiles;
   const size_t head = (size_t)bh * N * D;
   const unsigned head_bytes = (unsigned)N * D * 2;
   const int key = kt * kBwdKV + wave * 32 + l32;  // this lane's key (column of every accumulator)
@@ -330,11 +341,12 @@ void bwd_dq_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ Kg,
   auto kbuf = [&](int s) { return lds + s * 2 * T::kKTBytes; };
   auto vbuf = [&](int s) { return lds + s * 2 * T::kKTBytes + T::kKTBytes; };
 
-  // work item: query tile qt of head bh, the longest causal items (last
-  // query tiles) first
-  const int bh_count = gridDim.x / q_tiles;
-  const int r = blockIdx.x / bh_count;
-  const int bh = blockIdx.x - r * bh_count;
+  // work item: query tile qt of head bh, head-major over XCD-local logical
+  // indices (a head's K and V tiles are re-read by all its query tiles, from
+  // one L2); within a head the longest causal items (last query tiles) first
+  const int lw = xcd_local_index(blockIdx.x, gridDim.x);
+  const int bh = lw / q_tiles;
+  const int r = lw - bh * q_tiles;
   const int qt = CAUSAL ? q_tiles - 1 - r : r;
   const size_t head = (size_t)bh * N * D;
   const unsigned head_bytes = (unsigned)N * D * 2;
