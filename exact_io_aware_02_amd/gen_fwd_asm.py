@@ -493,7 +493,15 @@ def rescale_block(st, label):
 def step(st, parity, causal, kind, label):
     """Tile step j (parity = j & 1, j in s[S_J]).  kind: 'full' (PV of j-1,
     QK of j+1, softmax of j), 'last' (PV of j-1, softmax of j), 'first'
-    (j = 0: QK of 1, softmax of 0)."""
+    (j = 0: QK of 1, softmax of 0).
+
+    Causal: the wavefront's rows qw0 .. qw0 + 63 end in its diagonal tile
+    dj = qw0 / 64, and tiles after it get zero weights ("CMU 10-423 Lecture
+    18", section 4.3: work wholly above the diagonal is skipped).  So from
+    j = dj on the products with K_{j+1} are skipped, and from j = dj + 2 on
+    the whole step (PV of a zero W_{j-1}, the softmax of a masked tile): the
+    wavefront then only issues its share of the tile loads and joins the
+    barrier, which the other wavefronts of the workgroup still need."""
     j_odd = parity
     # top: own loads landed, every wavefront done with step j-1's buffers.
     # Step 0 reads only K_1, waited for before S_0; V_0 (and the previous
@@ -511,6 +519,32 @@ def step(st, parity, causal, kind, label):
         # V_j into V buffer j & 1, last read (V_{j-2}) in step j-1
         tile_rsrc(st.emit, "v", S_J, S_RV)
         groups += dma_groups("v", KV_LDS[2 + j_odd], S_RV)
+    if not causal or kind == "first":
+        step_body(st, j_odd, causal, kind, label, groups)
+        return
+    # 64 j - qw0: >= 128 from j = dj + 2 on, >= 0 from j = dj on
+    st.emit(f"s_lshl_b32 s{S_T1}, s{S_J}, 6")
+    st.emit(f"s_sub_u32 s{S_T1}, s{S_T1}, %[qw0]")
+    st.emit(f"s_cmp_ge_i32 s{S_T1}, 128")
+    st.emit(f"s_cbranch_scc1 {label}_dead_%=")
+    if kind == "full":
+        st.emit(f"s_cmp_ge_i32 s{S_T1}, 0")
+        st.emit(f"s_cbranch_scc1 {label}_pvo_%=")
+    step_body(st, j_odd, causal, kind, label, groups)
+    st.emit(f"s_branch {label}_join_%=")
+    if kind == "full":
+        st.emit(f"{label}_pvo_%=:")
+        step_body(st, j_odd, causal, "last", f"{label}p", groups)
+        st.emit(f"s_branch {label}_join_%=")
+    st.emit(f"{label}_dead_%=:")
+    for g in groups:
+        for ins in g:
+            st.emit(ins)
+    st.emit(f"{label}_join_%=:")
+
+
+def step_body(st, j_odd, causal, kind, label, groups):
+    """A step's mask, products, softmax and conditional rescale (see step)."""
     mask_block(st, j_odd, causal, f"{label}_mask")
     valu = softmax_ops(j_odd, j_odd, fast=(kind != "first"))
     if kind == "full":
@@ -575,6 +609,30 @@ def prefetch_setup(e):
         e(f"s_sub_u32 s{r + 2}, %[nhb], s{S_SOFF}")
         e(f"s_cselect_b32 s{r + 2}, 0, s{r + 2}")
         e(f"s_mov_b32 s{r + 3}, 0x20000")
+
+
+def final_block(st, par, causal, label):
+    """U += V_{n-1} W_{n-1} from buffers par (j = n - 1 in s[S_J]) while the
+    next item's Q, K_0, K_1 load.  Causal: a wavefront whose rows end before
+    tile n - 1 (64 (n - 1) >= qw0 + 64) has W_{n-1} = 0 and only issues the
+    loads."""
+    e = st.emit
+    e("s_waitcnt vmcnt(0) lgkmcnt(0)")
+    e("s_barrier")
+    prefetch_setup(e)
+    if causal:
+        e(f"s_lshl_b32 s{S_T1}, s{S_J}, 6")
+        e(f"s_sub_u32 s{S_T1}, s{S_T1}, %[qw0]")
+        e(f"s_cmp_ge_i32 s{S_T1}, 64")
+        e(f"s_cbranch_scc1 {label}_dead_%=")
+    st.block(pv_frags(par, par), [], groups=prefetch_groups())
+    if causal:
+        e(f"s_branch {label}_join_%=")
+        e(f"{label}_dead_%=:")
+        for g in prefetch_groups():
+            for ins in g:
+                e(ins)
+        e(f"{label}_join_%=:")
 
 
 # VMEM instructions a wavefront issues between the prefetch of the next
@@ -662,18 +720,12 @@ def item_asm(causal):
     # is read after step n - 2)
     e("L_last1_%=:")
     step(st, 1, causal, "last", "sl1")
-    e("s_waitcnt vmcnt(0) lgkmcnt(0)")
-    e("s_barrier")
-    prefetch_setup(e)
-    st.block(pv_frags(1, 1), [], groups=prefetch_groups())
+    final_block(st, 1, causal, "fb1")
     e("s_branch L_done_%=")
     e("L_last0_%=:")
     step(st, 0, causal, "last", "sl0")
     e("L_fin0_%=:")
-    e("s_waitcnt vmcnt(0) lgkmcnt(0)")
-    e("s_barrier")
-    prefetch_setup(e)
-    st.block(pv_frags(0, 0), [], groups=prefetch_groups())
+    final_block(st, 0, causal, "fb0")
     e("L_done_%=:")
     # epilogue: every wavefront done with the V buffers (the next item loads
     # V_0 at once); O = U / l into this wavefront's 64 staging rows (l summed

@@ -279,7 +279,7 @@ class _Machine:
     wavefronts run the same program, so a load is visible to every wavefront
     at the first barrier after this wavefront has waited for it."""
 
-    def __init__(self, g, n, pre, mem, item, wave=0, exec0_counts=True):
+    def __init__(self, g, n, pre, mem, item, wave=0, exec0_counts=True, qw0=0):
         self.g, self.n, self.mem, self.item = g, n, mem, item
         # the last 1 KiB block of a tile is loaded by wavefront 0 only; the
         # others issue that load with EXEC = 0, which may or may not count in
@@ -290,12 +290,13 @@ class _Machine:
         self.ops = {"%[n]": n, "%[pre]": pre, "%[wbase]": 0, "%[wave]": wave,
                     "%[kb]": 0, "%[vb]": self.vregion, "%[hb]": n * 16384, "%[nhb]": 1 << 24,
                     "%[klo]": 0, "%[vlo]": 0, "%[nklo]": 1 << 28, "%[nvlo]": 1 << 28, "%[khi]": 0, "%[vhi]": 0,
-                    "%[nkhi]": 0, "%[nvhi]": 0, "%[n_keys]": 64 * n, "%[qw0]": 0, "%[c]": 0, "%[theta]": 0}
+                    "%[nkhi]": 0, "%[nvhi]": 0, "%[n_keys]": 64 * n, "%[qw0]": qw0, "%[c]": 0, "%[theta]": 0}
         self.s = {}
         self.v = {}
         self.slots = {}   # AGPR slot -> tag of the data read into it
         self.fin = False
         self.barriers = 0      # the item's first block (S_0 = K_0 Q^T) follows its first barrier
+        self.pv_tiles = set()  # V tiles multiplied into U
         self.errors = []
 
     def val(self, x):
@@ -399,6 +400,7 @@ class _Machine:
                     want = ("K", self.item, j + 1 if par == (j + 1) % 2 else j)
                 else:                           # U += V W: V tile j - 1 (the last block: n - 1)
                     want = ("V", self.item, self.n - 1 if self.fin else j - 1)
+                    self.pv_tiles.add(want[2])
                 if self.slots.get(slot) != want:
                     self.errors.append((ln, self.slots.get(slot), want))
         return self.errors
@@ -440,7 +442,7 @@ class _Memory:
         return vis[-1] if vis else None
 
 
-@pytest.mark.parametrize("wave,exec0_counts", [(0, True), (1, True), (1, False)])
+@pytest.mark.parametrize("wave,exec0_counts", [(0, True), (1, True), (1, False), (2, True), (3, False)])
 @pytest.mark.parametrize("causal", [False, True])
 def test_lds_buffers_hold_the_tiles_each_product_reads(causal, wave, exec0_counts):
     """Sequences of items of 1 to 9 tiles, in a persistent workgroup's order
@@ -450,13 +452,23 @@ def test_lds_buffers_hold_the_tiles_each_product_reads(causal, wave, exec0_count
     read races a load still in flight."""
     g = _gen()
     prog = g.item_asm(causal)
-    for lengths in ([1, 1, 1, 1], [2, 3, 4, 5], [9, 1, 2, 7, 3], [5, 5, 5], [3, 8, 6, 2, 1, 4], [7]):
+    if causal:
+        # query tiles qt of 256 rows: n = 4 qt + 4 tiles, this wavefront's
+        # rows start at 256 qt + 64 wave (its diagonal tile is 4 qt + wave)
+        runs = [[(4 * qt + 4, 256 * qt + 64 * wave) for qt in qts] for qts in ([0, 3, 1, 2], [7, 0], [2, 2, 5])]
+    else:
+        runs = [[(n, 0) for n in lengths]
+                for lengths in ([1, 1, 1, 1], [2, 3, 4, 5], [9, 1, 2, 7, 3], [5, 5, 5], [3, 8, 6, 2, 1, 4], [7])]
+    for items in runs:
         mem = _Memory()
-        for i, n in enumerate(lengths):
-            m = _Machine(g, n, int(i > 0), mem, i, wave, exec0_counts)
+        for i, (n, qw0) in enumerate(items):
+            m = _Machine(g, n, int(i > 0), mem, i, wave, exec0_counts, qw0)
             errs = m.run(prog)
-            assert not errs, (lengths, i, errs[:3])
-        assert not mem.errors, (lengths, mem.errors[:3])
+            assert not errs, (items, i, errs[:3])
+            if causal:
+                # every product of a tile up to the diagonal one ran, none after it
+                assert m.pv_tiles == set(range(min(n, qw0 // 64 + 1))), (items, i, sorted(m.pv_tiles))
+        assert not mem.errors, (items, mem.errors[:3])
 
 
 def test_buffer_checker_catches_planted_mistakes():
