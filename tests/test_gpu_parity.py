@@ -161,19 +161,20 @@ def test_bf16_ragged_tail_reads_nothing_past_the_head(N, d):
 
 @pytest.mark.parametrize("causal", [True, False])
 @pytest.mark.parametrize("B,H,N", [(2, 200, 50), (1, 300, 300), (1, 520, 129), (3, 100, 700),
-                                   (1, 257, 513)])
+                                   (1, 257, 513), (1, 3, 2113)])
 def test_bf16_many_items_per_workgroup(B, H, N, causal):
     """At d = 128 launches keep at most one workgroup per compute unit, so
-    with many heads each workgroup runs a sequence of query tiles whose heads
-    change from one to the next.  Causal: the next tile's Q and first K/V
-    tiles are staged during the current one and the previous tile's output
-    is stored inside the next.  Non-causal: an item's last product block
-    loads the next item's Q, K_0 and K_1, and the next item waits for them
-    behind the previous item's stores.  Covers single-tile items (N <= 64:
-    every step is an item boundary), ragged last tiles, a grid with fewer
-    items than compute units in its last round (257 x 3 tiles over 256
-    workgroups) and mixes of long and short items; every head and row is
-    compared."""
+    with many heads each workgroup runs a sequence of query tiles (causal:
+    pairs of them) whose heads change from one to the next.  An item's last
+    product block loads the next item's Q, K_0 and K_1, and the next item
+    waits for them behind the previous item's stores.  Causal: a wavefront
+    skips the products of tiles after its rows, whole steps two tiles past
+    its diagonal one, and the final block when the last tile is after its
+    rows.  Covers single-tile items (N <= 64: every step is an item
+    boundary), ragged last tiles, a grid with fewer items than compute units
+    in its last round (257 x 3 tiles over 256 workgroups), long items with
+    a ragged tail (N = 2113: 9 query tiles, up to 34 steps) and mixes of long
+    and short items; every head and row is compared."""
     fa = _fa()
     _say("bf16 many items", B, H, N, "causal" if causal else "non-causal")
     shape = (B, H, N, 128)
