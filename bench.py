@@ -112,6 +112,8 @@ def cpu_baseline(Q, K, V, seconds, torch):
         "value": flops / spent / 1e12,
         "unit": "TFLOP/s",
         "cores": int(cores),
+        "cpu_count": os.cpu_count(),
+        "affinity": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None,
         "kind": "oracle",
         "sample": f"{heads} of {H} heads of prefill_8k (all {N} query rows each), float64 numpy",
         "seconds": round(spent, 3),
@@ -281,8 +283,10 @@ def main():
         evs.append(e)
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / K_
-    fwd_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / K_
-    dec_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / K_
+    fwd_t = sorted(e[0].elapsed_time(e[1]) for e in evs)
+    dec_t = sorted(e[1].elapsed_time(e[2]) for e in evs)
+    fwd_ms = sum(fwd_t) / K_
+    dec_ms = sum(dec_t) / K_
     log(f"fa_fwd {fwd_ms:.4f} ms, fa_decode {dec_ms * 1e3:.2f} us, wall/step {wall_ms:.4f} ms")
 
     flops = 4.0 * B * H * N * N * d
@@ -322,11 +326,15 @@ def main():
             "traffic": _traffic(None),
             "kernel": "fwd_bf16_asm_kernel<false>",
             "ms_per_launch": round(fwd_ms, 5),
+            "ms_per_launch_median": round(fwd_t[K_ // 2], 5),
+            "ms_per_launch_min": round(fwd_t[0], 5),
         },
         "decode": {
             "value": round(dec_gbs, 1),
             "unit": "GB/s",
             "us_per_step": round(dec_ms * 1e3, 2),
+            "us_per_step_median": round(dec_t[K_ // 2] * 1e3, 2),
+            "us_per_step_min": round(dec_t[0] * 1e3, 2),
             "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": PEAK_HBM_GBS,
                          "unit": "GB/s", "frac": round(dec_gbs / PEAK_HBM_GBS, 4),
                          "bytes_per_step": dec_bytes},
