@@ -23,8 +23,10 @@
 //    values without spilling, so one query tile's loop is assembly generated
 //    by gen_fwd_asm.py with one fixed register for every value.
 //  * Causal: tiles wholly after a query tile are never visited; a
-//    wavefront masks its diagonal tile, and a tile wholly after its 64 rows
-//    (inside the query tile's range) gets zero weights through m c = +inf.
+//    wavefront masks its diagonal tile, and skips the products of tiles
+//    wholly after its 64 rows (inside the query tile's range), issuing only
+//    its share of their loads and joining the barriers; a skipped tile's
+//    softmax, where it still runs, gets zero weights through m c = +inf.
 //  * Persistent workgroups, one per compute unit: during an item's last
 //    product block the next item's Q fragments and first two K tiles load
 //    into the registers and K buffers that block no longer reads, and the

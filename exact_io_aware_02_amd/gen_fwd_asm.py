@@ -424,7 +424,8 @@ def mask_block(st, sbuf, causal, label):
         kept, the upper-right one dropped, and the two diagonal blocks compare
         c against %[dg] = l32 - 4 g;
       * a tile wholly after the rows (kbase > qw0): every weight is zero, which
-        m c = +inf gives for the whole tile (restored after the step)."""
+        m c = +inf gives for the whole tile (restored after the step); step
+        runs this only for the first such tile, and skips the rest."""
     st.emit(f"s_lshl_b32 s{S_KB}, s{S_J}, 6")
     st.emit(f"s_add_u32 s{S_T1}, s{S_KB}, 64")
     st.emit(f"s_cmp_gt_u32 s{S_T1}, %[n_keys]")
