@@ -66,6 +66,26 @@ def _timed(fn, steps, warmup, torch):
     return sum(a.elapsed_time(b) for a, b in evs) / steps
 
 
+def _interleaved(fa, shares, fn, rounds, per, torch):
+    """Mean ms per launch of fn under each exponential share, the shares
+    taking turns within each round (so that clock drift hits all alike)."""
+    tot = {k: 0.0 for k in shares}
+    for _ in range(rounds):
+        for k in shares:
+            fa.fa_set_fwd_exp2_poly(k)
+            fn()  # the first launch after a switch is not timed
+            evs = []
+            for _ in range(per):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                fn()
+                b.record()
+                evs.append((a, b))
+            torch.cuda.synchronize()
+            tot[k] += sum(a.elapsed_time(b) for a, b in evs)
+    return {k: v / (rounds * per) for k, v in tot.items()}
+
+
 def _traffic(n_launch_bytes_alg):
     """Measured HBM bytes per fa_fwd launch from committed rocprofv3 counters,
     valid only while the kernel source is unchanged."""
@@ -204,6 +224,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip causal_4k and decode_varlen")
     ap.add_argument("--num-splits", type=int, default=0, help="decode splits (0 = automatic)")
+    ap.add_argument("--exp2-poly", type=int, default=0, choices=(0, 4, 8, 16),
+                    help="exponentials per 64 that the d = 128 forward evaluates by polynomial in the "
+                         "timed steps (0: hardware exponential only, the library default)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="before timing, run one plain device copy of this many MiB (calibrates "
                          "HBM byte counters under rocprofv3)")
@@ -239,6 +262,8 @@ def main():
         torch.cuda.synchronize()
         del src, dst
         log(f"copy probe: {args.copy_probe_mib} MiB read + {args.copy_probe_mib} MiB written")
+
+    fa.fa_set_fwd_exp2_poly(args.exp2_poly)
 
     # ---------------- inputs (resident in HBM before timing)
     cfg = synth.WORKLOADS["prefill_8k"]
@@ -313,7 +338,7 @@ def main():
             "workload": "prefill_8k (B=1,H=32,N=8192,d=128, non-causal) + decode_32k (B=1,H=32,L=32768,d=128)",
             "prefill": {"B": B, "H": H, "N": N, "d": d, "causal": False,
                         "block_rows": plan["block_rows"], "block_cols": plan["block_cols"],
-                        "workgroups": plan["workgroups"]},
+                        "workgroups": plan["workgroups"], "exp2_poly_per64": args.exp2_poly},
             "decode": {"B": Bd, "H": Hd, "L": int(lengths[0]), "d": dd,
                        "num_splits": splits if splits else f"auto ({cus} CUs)", "rotating_caches": n_rot},
         },
@@ -377,8 +402,21 @@ def main():
             "frac_of_peak": round(tf_c / PEAK_BF16_TFLOPS, 4),
             "flops_algorithmic": alg, "flops_executed_tiles": executed,
         }
-        del Qc, Kc3, Vc3, Oc, Lc
         log(f"causal_4k {ms_c:.4f} ms -> {tf_c:.1f} TFLOP/s")
+
+        # exponentials by polynomial: every share against the hardware
+        # exponential, interleaved launch by launch on both prefill workloads
+        shares = (0, 4, 8, 16)
+        runs = {"prefill_8k": (lambda: fa.fa_fwd(Q, K, V, O, L, causal=False, scale=scale), flops),
+                "causal_4k": (lambda: fa.fa_fwd(Qc, Kc3, Vc3, Oc, Lc, causal=True), alg)}
+        result["exp2_poly"] = {"unit": "TFLOP/s", "note": "exponentials per 64 by polynomial on the "
+                               "multiply-add units; shares timed in turn, 8 rounds of 5 launches each"}
+        for wname, (fn, fl) in runs.items():
+            ms = _interleaved(fa, shares, fn, 8, 5, torch)
+            result["exp2_poly"][wname] = {str(k): round(fl / (v * 1e-3) / 1e12, 1) for k, v in ms.items()}
+            log(f"exp2 poly {wname} {result['exp2_poly'][wname]}")
+        fa.fa_set_fwd_exp2_poly(args.exp2_poly)
+        del Qc, Kc3, Vc3, Oc, Lc
 
         qv, Kv, Vv, lv = synth.decode_inputs("decode_varlen", dev)
         Lv = torch.tensor(lv, dtype=torch.int32, device=dev)

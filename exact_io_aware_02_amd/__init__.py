@@ -30,6 +30,8 @@ from ._binding import (  # noqa: F401
     fa_fwd,
     fa_fwd_f32,
     fa_fwd_plan,
+    fa_get_fwd_exp2_poly,
+    fa_set_fwd_exp2_poly,
     fa_probe_hbm_read,
     fa_probe_mfma_bf16,
     fa_release_workspace,

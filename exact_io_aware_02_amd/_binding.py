@@ -66,6 +66,8 @@ def _load():
     sig = {
         "fa_fwd": (I, [P, P, P, P, P, I, I, I, I, I, F, P]),
         "fa_fwd_f32": (I, [P, P, P, P, P, I, I, I, I, I, F, P]),
+        "fa_set_fwd_exp2_poly": (I, [I]),
+        "fa_get_fwd_exp2_poly": (I, []),
         "fa_decode": (I, [P, P, P, P, I, I, P, I, I, P]),
         "fa_bwd": (I, [P, P, P, P, P, P, P, P, P, I, I, I, I, I, F, P, Z, P]),
         "fa_bwd_workspace_bytes": (Z, [I, I, I]),
@@ -98,6 +100,8 @@ lib = _load()
 EXPORTED = (
     "fa_fwd",
     "fa_fwd_f32",
+    "fa_set_fwd_exp2_poly",
+    "fa_get_fwd_exp2_poly",
     "fa_bwd",
     "fa_bwd_workspace_bytes",
     "fa_decode",
@@ -204,6 +208,19 @@ def fa_fwd(Q, K, V, O, L=None, causal=False, scale=None, stream=None):
     _check(lib.fa_fwd(_ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(L), B, H, N, d, int(causal),
                       float(scale), _stream_ptr(stream)))
     return O, L
+
+
+def fa_set_fwd_exp2_poly(per64):
+    """Exponentials per 64 that the d = 128 bf16 forward evaluates by a
+    polynomial on the multiply-add units (0, 4, 8 or 16; 0 is the default).
+    Returns the previous setting."""
+    prev = lib.fa_get_fwd_exp2_poly()
+    _check(lib.fa_set_fwd_exp2_poly(int(per64)))
+    return prev
+
+
+def fa_get_fwd_exp2_poly():
+    return lib.fa_get_fwd_exp2_poly()
 
 
 def fa_bwd_workspace_bytes(B, H, N):

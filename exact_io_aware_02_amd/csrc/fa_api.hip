@@ -6,6 +6,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <atomic>
 #include <map>
 #include <mutex>
 #include <string>
@@ -292,6 +293,18 @@ const char* fa_last_error(void) { return g_last_error.c_str(); }
 
 int fa_version(void) { return (1 << 16) | 0; }
 
+// exponentials per 64 that the d = 128 bf16 forward evaluates by polynomial
+static std::atomic<int> g_fwd_exp2_poly{0};
+
+int fa_set_fwd_exp2_poly(int per64) {
+  if (per64 != 0 && per64 != 4 && per64 != 8 && per64 != 16)
+    return fail(FA_ERR_INVALID_ARG, "exponentials per 64 by polynomial must be 0, 4, 8 or 16 (got %d)", per64);
+  g_fwd_exp2_poly.store(per64, std::memory_order_relaxed);
+  return ok();
+}
+
+int fa_get_fwd_exp2_poly(void) { return g_fwd_exp2_poly.load(std::memory_order_relaxed); }
+
 int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* L, int B, int H, int N,
            int d, int causal, float scale, void* stream) {
   int st = check_fwd(Q, K, V, O, L, B, H, N, d, causal, scale, 2, fa::kFwdBR);
@@ -299,7 +312,8 @@ int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* L, int B
   int cus = 0;
   if ((st = cu_count(&cus)) != FA_OK) return st;
   fa::FwdArgs a{Q, K, V, O, L, B, H, N, causal, scale,
-                (int)fa::fwd_grid(fa::fwd_units(B, H, N, causal), d, causal, cus)};
+                (int)fa::fwd_grid(fa::fwd_units(B, H, N, causal), d, causal, cus),
+                g_fwd_exp2_poly.load(std::memory_order_relaxed)};
   hipError_t e = fa::launch_fwd_bf16(a, d, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "fa_fwd launch");
   return ok();

@@ -56,7 +56,10 @@ constexpr int kLds = kKV + kWaves * 64 * kStride;
 static_assert(kBR == kFwdBR && kBC == kFwdBC, "tiles must match the planner");
 static_assert(kKV == fwd_lds_bytes(D) && kLds == fwd_asm_lds_bytes(), "LDS size must match the planner");
 
-template <bool CAUSAL>
+// POLY: exponentials per 64 of a tile evaluated by a polynomial on the
+// multiply-add units instead of v_exp_f32 (0, or one of the generator's
+// shares)
+template <bool CAUSAL, int POLY>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void fwd_bf16_asm_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ Kg,
                          const __bf16* __restrict__ Vg, __bf16* __restrict__ Og,
@@ -179,12 +182,29 @@ void fwd_bf16_asm_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict
     [qrsrc] "s"(q_rsrc), [nqrsrc] "s"(nq_rsrc), [orsrc] "s"(o_rsrc), [lrsrc] "s"(l_rsrc), [klo] "s"(klo),        \
     [khi] "s"(khi), [vlo] "s"(vlo), [vhi] "s"(vhi), [hb] "s"(head_bytes), [nklo] "s"(nklo), [nkhi] "s"(nkhi),    \
     [nhb] "s"(nhb), [n] "s"(n), [wave] "s"(wave), [wbase] "s"(wbase), [n_keys] "s"(N), [qw0] "s"(qw0),           \
-    [pre] "s"(pre)                                                                                               \
-  : FA_ASM_CLOBBERS
-    if constexpr (CAUSAL)
-      asm volatile(FA_ASM_ITEM_CAUSAL FA_ASM_OPERANDS);
-    else
-      asm volatile(FA_ASM_ITEM FA_ASM_OPERANDS);
+    [pre] "s"(pre)
+    if constexpr (POLY == 0) {
+      if constexpr (CAUSAL)
+        asm volatile(FA_ASM_ITEM_CAUSAL FA_ASM_OPERANDS : FA_ASM_CLOBBERS);
+      else
+        asm volatile(FA_ASM_ITEM FA_ASM_OPERANDS : FA_ASM_CLOBBERS);
+    } else if constexpr (POLY == 4) {
+      if constexpr (CAUSAL)
+        asm volatile(FA_ASM_ITEM_CAUSAL_POLY4 FA_ASM_OPERANDS : FA_ASM_CLOBBERS_POLY);
+      else
+        asm volatile(FA_ASM_ITEM_POLY4 FA_ASM_OPERANDS : FA_ASM_CLOBBERS_POLY);
+    } else if constexpr (POLY == 8) {
+      if constexpr (CAUSAL)
+        asm volatile(FA_ASM_ITEM_CAUSAL_POLY8 FA_ASM_OPERANDS : FA_ASM_CLOBBERS_POLY);
+      else
+        asm volatile(FA_ASM_ITEM_POLY8 FA_ASM_OPERANDS : FA_ASM_CLOBBERS_POLY);
+    } else {
+      static_assert(POLY == 16, "a share the generator builds");
+      if constexpr (CAUSAL)
+        asm volatile(FA_ASM_ITEM_CAUSAL_POLY16 FA_ASM_OPERANDS : FA_ASM_CLOBBERS_POLY);
+      else
+        asm volatile(FA_ASM_ITEM_POLY16 FA_ASM_OPERANDS : FA_ASM_CLOBBERS_POLY);
+    }
 #undef FA_ASM_OPERANDS
     pre = 1;
     unit = nunit;
@@ -195,21 +215,31 @@ void fwd_bf16_asm_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
-template <bool CAUSAL>
+template <bool CAUSAL, int POLY>
 hipError_t launch(const FwdArgs& a, hipStream_t stream) {
   const int q_tiles = (a.N + kBR - 1) / kBR;
   const int64_t units = fwd_units(a.B, a.H, a.N, a.causal);
-  hipLaunchKernelGGL((fwd_bf16_asm_kernel<CAUSAL>), dim3((unsigned)a.grid), dim3(kThreads), 0, stream,
+  hipLaunchKernelGGL((fwd_bf16_asm_kernel<CAUSAL, POLY>), dim3((unsigned)a.grid), dim3(kThreads), 0, stream,
                      static_cast<const __bf16*>(a.Q), static_cast<const __bf16*>(a.K),
                      static_cast<const __bf16*>(a.V), static_cast<__bf16*>(a.O), a.L, a.N, q_tiles,
                      (int)units, a.scale);
   return hipGetLastError();
 }
 
+template <int POLY>
+hipError_t launch_poly(const FwdArgs& a, hipStream_t stream) {
+  return a.causal ? launch<true, POLY>(a, stream) : launch<false, POLY>(a, stream);
+}
+
 }  // namespace
 
 hipError_t launch_fwd_bf16_asm(const FwdArgs& a, hipStream_t stream) {
-  return a.causal ? launch<true>(a, stream) : launch<false>(a, stream);
+  switch (a.exp2_poly) {
+    case 4: return launch_poly<4>(a, stream);
+    case 8: return launch_poly<8>(a, stream);
+    case 16: return launch_poly<16>(a, stream);
+    default: return launch_poly<0>(a, stream);
+  }
 }
 
 }  // namespace fa

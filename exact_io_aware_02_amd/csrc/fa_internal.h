@@ -65,6 +65,7 @@ struct FwdArgs {
   int causal;
   float scale;
   int grid;  // bf16 prefill: persistent workgroups, 1 <= grid <= fwd_units
+  int exp2_poly = 0;  // d = 128 bf16: exponentials per 64 by polynomial (0, 4, 8, 16)
 };
 
 struct BwdArgs {

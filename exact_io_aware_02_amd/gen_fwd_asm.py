@@ -85,6 +85,22 @@ LOOKAHEAD = 6
 LOAD_SPREAD = 0.5
 VALU_LEAD = 8                # softmax instructions issued before a step's first MFMA
 
+# Exponentials given to a polynomial (the share of "Infra: Flash Attention",
+# section "FlashAttention-4", that runs on the multiply-add units): with
+# poly = k > 0, k of the 64 exponentials per lane of a tile are
+# 2^x = 2^floor(x) p(x - floor(x)), p the cubic with p(0) = 1 of least
+# maximum relative error against 2^f on [0, 1] (fitted by linear programming
+# over 20,001 points; 8.6e-5, checked in float32 Horner order by the CPU
+# tests), floor(x) added to the exponent by v_ldexp_f32.  x is clamped at
+# -200 first, so masked scores (-inf) give exactly 0, as v_exp_f32 does.
+POLY_SHARES = (4, 8, 16)     # variants built besides 0 (v_exp_f32 only)
+POLY_C1 = 0x3F31F335         # 0.695117...
+POLY_C2 = 0x3E691B63         # 0.227643...
+POLY_C3 = 0x3D9DD5D8         # 0.077068...
+POLY_CLAMP = 0xC3480000      # -200.0
+V_POLY_P = 224               # Horner accumulator (the query blocks' pairs run one after the other)
+V_POLY_C2 = 225              # c2 (v_fmamk_f32 takes one literal)
+
 # SGPRs used inside (declared as clobbers)
 S_J = 40        # tile index j
 S_T1 = 41
@@ -143,7 +159,7 @@ def interleave_lists(lists):
     return out
 
 
-def softmax_ops(sbuf, wbuf, fast=False):
+def softmax_ops(sbuf, wbuf, fast=False, poly=0):
     """VALU instructions of the softmax of score tile sbuf into W tile wbuf:
     row max, the conditional move of the base (threshold theta in raw score
     units), W = exp2(c S - c m) in bf16, the fp32 row sums, l = alpha l + sum.
@@ -160,13 +176,15 @@ def softmax_ops(sbuf, wbuf, fast=False):
     fast: W relative to the current base without forming the row max; l is
     left alone and the tile's per-lane sums are left in psum[0] and psum[4].
     If no sum exceeds 2^8, no weight did either, and the result is what the
-    full version gives when the base does not move (alpha = 1)."""
+    full version gives when the base does not move (alpha = 1).
+
+    poly: exponentials per 64 given to the polynomial (exp_ops)."""
     sb = S_BUF[sbuf]
     ops = []
     pair_tmp = [(TMP0 + 4 * i, TMP0 + 4 * i + 1) for i in range(4)]          # banks 0, 1
     psum = [TMP0 + 4 * (i // 2) + 2 + (i & 1) for i in range(8)]             # banks 2, 3
     if fast:
-        return exp_ops(sb, wbuf, pair_tmp, psum)
+        return exp_ops(sb, wbuf, pair_tmp, psum, poly)
     # row max: per (query block, 32-key block) two chains, over the scores in
     # banks {0, 2} (accumulator in bank 1 or 3) and in banks {1, 3}
     # (accumulator in bank 0 or 2)
@@ -214,17 +232,39 @@ def softmax_ops(sbuf, wbuf, fast=False):
             f"v_cndmask_b32_e64 v{al}, 1.0, v{t}, s[{mv}:{mv + 1}]",  # alpha
         ])
     ops += interleave_lists(thr)
-    ops += exp_ops(sb, wbuf, pair_tmp, psum)
+    ops += exp_ops(sb, wbuf, pair_tmp, psum, poly)
     for qb in range(2):
         ops.append(f"v_fma_f32 v{V_L[qb]}, v{V_AL[qb]}, v{V_L[qb]}, v{psum[4 * qb]}")
     return ops
 
 
-def exp_ops(sb, wbuf, pair_tmp, psum):
+def exp2_poly(x, f, p):
+    """x <- 2^x on the multiply-add units: clamp, fraction f and floor (in
+    place, as an integer), Horner p(f) = 1 + f (c1 + f (c2 + f c3)), then
+    p 2^floor by the exponent.  f and p are temporaries."""
+    return [
+        f"v_max_f32 v{x}, {POLY_CLAMP:#x}, v{x}",
+        f"v_fract_f32 v{f}, v{x}",
+        f"v_cvt_flr_i32_f32 v{x}, v{x}",
+        f"v_fmamk_f32 v{p}, v{f}, {POLY_C3:#x}, v{V_POLY_C2}",
+        f"v_fmaak_f32 v{p}, v{p}, v{f}, {POLY_C1:#x}",
+        f"v_fma_f32 v{p}, v{p}, v{f}, 1.0",
+        f"v_ldexp_f32 v{x}, v{p}, v{x}",
+    ]
+
+
+def exp_ops(sb, wbuf, pair_tmp, psum, poly=0):
     """W = exp2(c S - c m) for a score tile: per pair of scores two FMAs, two
     exponentials (each read at least one instruction later), two adds into
     the partial sum of the pair's 8-key group, one bf16 pack; the two query
-    blocks alternate.  Leaves the per-lane tile sums in psum[0], psum[4]."""
+    blocks alternate pair by pair.  Leaves the per-lane tile sums in psum[0],
+    psum[4].
+
+    poly = k: the second exponential of every (32 / k)-th pair of a query
+    block is exp2_poly, with the pair's W register (written only by the
+    pack) as its fraction temporary."""
+    assert poly == 0 or poly in POLY_SHARES
+    every = 32 // poly if poly else 0
     ops = []
     seqs = {0: [], 1: []}
     k_pair = 0
@@ -238,17 +278,18 @@ def exp_ops(sb, wbuf, pair_tmp, psum):
                 a, b = pair_tmp[k_pair % 4]
                 k_pair += 1
                 ps = psum[4 * qb + ks]
-                seqs[qb] += [
+                by_poly = every and (4 * ks + k) % every == every - 1
+                seqs[qb].append([
                     f"v_fma_f32 v{a}, v{src}, s{S_C}, -v{mcx}",
                     f"v_fma_f32 v{b}, v{src + 1}, s{S_C}, -v{mcx}",
                     f"v_exp_f32 v{a}, v{a}",
-                    f"v_exp_f32 v{b}, v{b}",
+                    *(exp2_poly(b, w + k, V_POLY_P) if by_poly else [f"v_exp_f32 v{b}, v{b}"]),
                     f"v_add_f32 v{ps}, 0, v{a}" if k == 0 else f"v_add_f32 v{ps}, v{ps}, v{a}",
                     f"v_add_f32 v{ps}, v{ps}, v{b}",
                     f"v_cvt_pk_bf16_f32 v{w + k}, v{a}, v{b}",
-                ]
-    for i in range(0, len(seqs[0]), 7):
-        ops += seqs[0][i:i + 7] + seqs[1][i:i + 7]
+                ])
+    for c0, c1 in zip(seqs[0], seqs[1]):
+        ops += c0 + c1
     for qb in range(2):
         p = psum[4 * qb:4 * qb + 4]
         ops += [f"v_add_f32 v{p[0]}, v{p[0]}, v{p[1]}", f"v_add_f32 v{p[2]}, v{p[2]}, v{p[3]}"]
@@ -263,8 +304,9 @@ class Stream:
     LOOKAHEAD fragments ahead, lgkmcnt waits counted per read, and VALU
     instructions spread evenly between the MFMAs."""
 
-    def __init__(self):
+    def __init__(self, poly=0):
         self.out = []
+        self.poly = poly   # exponentials per 64 given to the polynomial
 
     def emit(self, s):
         self.out.append(s)
@@ -547,7 +589,7 @@ def step(st, parity, causal, kind, label):
 def step_body(st, j_odd, causal, kind, label, groups):
     """A step's mask, products, softmax and conditional rescale (see step)."""
     mask_block(st, j_odd, causal, f"{label}_mask")
-    valu = softmax_ops(j_odd, j_odd, fast=(kind != "first"))
+    valu = softmax_ops(j_odd, j_odd, fast=(kind != "first"), poly=st.poly)
     if kind == "full":
         frags = interleave(pv_frags(1 - j_odd, 1 - j_odd), qk_frags(1 - j_odd, 1 - j_odd))
     elif kind == "last":
@@ -576,7 +618,7 @@ def step_body(st, j_odd, causal, kind, label, groups):
         st.emit(f"v_add_f32 v{V_L[1]}, v{V_L[1]}, v{t1}")
         st.emit(f"s_branch {label}_done_%=")
         st.emit(f"{label}_slow_%=:")
-        for ins in softmax_ops(j_odd, j_odd):
+        for ins in softmax_ops(j_odd, j_odd, poly=st.poly):
             st.emit(ins)
         rescale_block(st, f"{label}_rs")
         st.emit(f"{label}_done_%=:")
@@ -643,14 +685,17 @@ def final_block(st, par, causal, label):
 VM_AFTER_PREFETCH = 16 + 2 + 4
 
 
-def item_asm(causal):
+def item_asm(causal, poly=0):
     """One query tile of a wavefront: the tile loop, then O and L stored.
     %[pre] = 1: Q, K_0, K_1 were prefetched by the previous item, which
     issued nothing but its stores after them.  Every item prefetches those of
-    the next one (%[nq*], %[nk*]; empty resources if there is none)."""
-    st = Stream()
+    the next one (%[nq*], %[nk*]; empty resources if there is none).
+    poly: exponentials per 64 of a tile computed by exp2_poly (0: none)."""
+    st = Stream(poly)
     e = st.emit
     e(f"s_mov_b32 s{S_M0}, m0")
+    if poly:
+        e(f"v_mov_b32 v{V_POLY_C2}, {POLY_C2:#x}")
     e(f"v_readfirstlane_b32 s{S_C}, %[c]")
     e(f"v_readfirstlane_b32 s{S_THETA}, %[theta]")
     e(f"s_mov_b32 s{S_256}, 0x43800000")
@@ -781,8 +826,10 @@ def item_asm(causal):
     return st.out
 
 
-def clobbers():
+def clobbers(poly=0):
     v = [f'"v{i}"' for i in range(0, ST + 16)]
+    if poly:
+        v += [f'"v{i}"' for i in (V_POLY_P, V_POLY_C2)]
     a = [f'"a{i}"' for i in range(256)]
     s = [f'"s{i}"' for i in SGPR_CLOBBERS]
     return ", ".join(v + a + s + ['"vcc"', '"scc"', '"memory"'])
@@ -791,13 +838,16 @@ def clobbers():
 def main(out):
     with open(out, "w") as f:
         f.write("// Generated by gen_fwd_asm.py; do not edit.\n#pragma once\n\n")
-        for name, causal in (("FA_ASM_ITEM", False), ("FA_ASM_ITEM_CAUSAL", True)):
-            body = item_asm(causal)
-            f.write(f"#define {name} \\\n")
-            for ins in body:
-                f.write(f'  "{ins}\\n" \\\n')
-            f.write('  ""\n\n')
+        for poly in (0, *POLY_SHARES):
+            sfx = f"_POLY{poly}" if poly else ""
+            for name, causal in (("FA_ASM_ITEM", False), ("FA_ASM_ITEM_CAUSAL", True)):
+                body = item_asm(causal, poly)
+                f.write(f"#define {name}{sfx} \\\n")
+                for ins in body:
+                    f.write(f'  "{ins}\\n" \\\n')
+                f.write('  ""\n\n')
         f.write(f"#define FA_ASM_CLOBBERS {clobbers()}\n")
+        f.write(f"#define FA_ASM_CLOBBERS_POLY {clobbers(1)}\n")
 
 
 if __name__ == "__main__":

@@ -99,6 +99,24 @@ int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* L, int B
            int N, int d, int causal, float scale, void* stream);
 
 /*
+ * fa_set_fwd_exp2_poly -- how many of the 64 exponentials per lane of a tile
+ * the d = 128 bf16 forward evaluates by a polynomial on the multiply-add
+ * units instead of the hardware exponential ([FA] "FlashAttention-4": part
+ * of the exponentials on the FMA units, with the share to be chosen and
+ * the approximation error to be evaluated).
+ *   per64 : 0 (the default: hardware exponential only), 4, 8 or 16.  The
+ *           polynomial is a cubic in the fraction of the exponent, maximum
+ *           relative error 8.6e-5 (below the bf16 rounding of the
+ *           probabilities), scaled by the integer part through the exponent.
+ * Process-wide; read by each later fa_fwd call (calls already enqueued keep
+ * their setting).  d = 64 and fa_fwd_f32 are not affected.
+ * Errors: FA_ERR_INVALID_ARG for any other value (the setting is unchanged).
+ * fa_get_fwd_exp2_poly returns the current setting.
+ */
+int fa_set_fwd_exp2_poly(int per64);
+int fa_get_fwd_exp2_poly(void);
+
+/*
  * fa_fwd_f32 -- the same contract with fp32 Q, K, V, O (device fp32
  * [B, H, N, d]); every operation is fp32 (no reduced-precision step).
  */

@@ -338,3 +338,22 @@ def test_probes_reject_invalid_arguments():
     assert lib.fa_probe_mfma_bf16(4, 0, A, None, None) == -1
     assert lib.fa_probe_mfma_bf16(4, 10, A, A + 4, None) == -1           # stamps misaligned
     assert lib.fa_probe_mfma_bf16(4, 10, A, A + 8, None) == -1           # stamps inside sink
+
+
+def test_exp2_poly_share_is_validated():
+    """fa_set_fwd_exp2_poly takes 0, 4, 8 or 16 exponentials per 64 and
+    leaves the setting unchanged on any other value."""
+    fa = _fa()
+    lib = fa.lib
+    assert lib.fa_get_fwd_exp2_poly() == 0
+    try:
+        for v in (4, 8, 16, 0):
+            assert lib.fa_set_fwd_exp2_poly(v) == 0
+            assert lib.fa_get_fwd_exp2_poly() == v
+        assert lib.fa_set_fwd_exp2_poly(8) == 0
+        for v in (-1, 1, 2, 3, 12, 32, 64):
+            assert lib.fa_set_fwd_exp2_poly(v) == -1
+            assert lib.fa_get_fwd_exp2_poly() == 8
+        assert "0, 4, 8 or 16" in fa.last_error()
+    finally:
+        lib.fa_set_fwd_exp2_poly(0)

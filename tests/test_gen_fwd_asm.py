@@ -81,10 +81,21 @@ def _wait_states(op, line):
     return 1
 
 
-@pytest.fixture(scope="module", params=[False, True], ids=["non-causal", "causal"])
+_VARIANTS = [(c, p) for p in (0, 4, 8, 16) for c in (False, True)]
+
+
+@pytest.fixture(scope="module", params=_VARIANTS,
+                ids=[("causal" if c else "non-causal") + (f"-poly{p}" if p else "") for c, p in _VARIANTS])
 def program(request):
+    """(generator, program) of one kernel variant; the generator's clobbers()
+    is bound to the variant's exponential share."""
     g = _gen()
-    return g, [ln for ln in g.item_asm(request.param)]
+    causal, poly = request.param
+    assert poly == 0 or poly in g.POLY_SHARES
+    prog = [ln for ln in g.item_asm(causal, poly)]
+    base_clobbers = g.clobbers
+    g.clobbers = lambda poly=poly: base_clobbers(poly)
+    return g, prog
 
 
 def test_register_homes_are_disjoint(program):
