@@ -66,19 +66,21 @@ def _timed(fn, steps, warmup, torch):
     return sum(a.elapsed_time(b) for a, b in evs) / steps
 
 
-def _interleaved(fa, shares, fn, rounds, per, torch):
-    """Mean ms per launch of fn under each exponential share, the shares
-    taking turns within each round (so that clock drift hits all alike)."""
-    tot = {k: 0.0 for k in shares}
+def _interleaved(variants, rounds, per, torch):
+    """Mean ms per launch of each variant {name: (setup, fn)}, the variants
+    taking turns within each round (so that clock drift hits all alike);
+    setup() runs before a variant's turn, and its first launch is not
+    timed."""
+    tot = {k: 0.0 for k in variants}
     for _ in range(rounds):
-        for k in shares:
-            fa.fa_set_fwd_exp2_poly(k)
-            fn()  # the first launch after a switch is not timed
+        for k, (setup, fn) in variants.items():
+            setup()
+            fn(0)
             evs = []
-            for _ in range(per):
+            for i in range(per):
                 a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 a.record()
-                fn()
+                fn(i + 1)
                 b.record()
                 evs.append((a, b))
             torch.cuda.synchronize()
@@ -407,16 +409,39 @@ def main():
         # exponentials by polynomial: every share against the hardware
         # exponential, interleaved launch by launch on both prefill workloads
         shares = (0, 4, 8, 16)
-        runs = {"prefill_8k": (lambda: fa.fa_fwd(Q, K, V, O, L, causal=False, scale=scale), flops),
-                "causal_4k": (lambda: fa.fa_fwd(Qc, Kc3, Vc3, Oc, Lc, causal=True), alg)}
+        runs = {"prefill_8k": (lambda i: fa.fa_fwd(Q, K, V, O, L, causal=False, scale=scale), flops),
+                "causal_4k": (lambda i: fa.fa_fwd(Qc, Kc3, Vc3, Oc, Lc, causal=True), alg)}
         result["exp2_poly"] = {"unit": "TFLOP/s", "note": "exponentials per 64 by polynomial on the "
                                "multiply-add units; shares timed in turn, 8 rounds of 5 launches each"}
         for wname, (fn, fl) in runs.items():
-            ms = _interleaved(fa, shares, fn, 8, 5, torch)
+            ms = _interleaved({k: (lambda k=k: fa.fa_set_fwd_exp2_poly(k), fn) for k in shares}, 8, 5, torch)
             result["exp2_poly"][wname] = {str(k): round(fl / (v * 1e-3) / 1e12, 1) for k, v in ms.items()}
             log(f"exp2 poly {wname} {result['exp2_poly'][wname]}")
         fa.fa_set_fwd_exp2_poly(args.exp2_poly)
         del Qc, Kc3, Vc3, Oc, Lc
+
+        # decode_32k in one launch (the last split workgroup merges) against
+        # split + combine, interleaved, both with caller workspaces
+        S_d = fa.fa_decode_plan(Bd, Hd, dd, splits)["num_splits"] if splits else 0
+        ws_ex = torch.empty(fa.fa_decode_workspace_bytes(Bd, Hd, dd, S_d), dtype=torch.uint8, device=dev)
+        ws_fu = torch.zeros(fa.fa_decode_fused_workspace_bytes(Bd, Hd, dd, S_d), dtype=torch.uint8, device=dev)
+
+        def dec_ex(i):
+            q, Kc, Vc, _ = caches[i % n_rot]
+            fa.fa_decode_ex(q, Kc, Vc, od, Lkv, ws_ex, num_splits=S_d)
+
+        def dec_fused(i):
+            q, Kc, Vc, _ = caches[i % n_rot]
+            fa.fa_decode_fused(q, Kc, Vc, od, Lkv, ws_fu, num_splits=S_d)
+
+        ms_d = _interleaved({"split_combine": (lambda: None, dec_ex), "fused": (lambda: None, dec_fused)},
+                            8, 8, torch)
+        result["decode"]["one_launch"] = {
+            "us_per_step": round(ms_d["fused"] * 1e3, 2), "two_launch_us_per_step": round(ms_d["split_combine"] * 1e3, 2),
+            "value": round(dec_bytes / (ms_d["fused"] * 1e-3) / 1e9, 1), "unit": "GB/s",
+            "note": "fa_decode_fused against fa_decode_ex, timed in turn, 8 rounds of 8 launches each"}
+        log(f"decode_32k one launch {ms_d['fused'] * 1e3:.2f} us against two {ms_d['split_combine'] * 1e3:.2f} us")
+        del ws_ex, ws_fu
 
         qv, Kv, Vv, lv = synth.decode_inputs("decode_varlen", dev)
         Lv = torch.tensor(lv, dtype=torch.int32, device=dev)

@@ -21,6 +21,8 @@ from ._binding import (  # noqa: F401
     fa_decode,
     fa_decode_chunk_tokens,
     fa_decode_ex,
+    fa_decode_fused,
+    fa_decode_fused_workspace_bytes,
     fa_decode_noalloc,
     fa_decode_noalloc_scratch_bytes,
     fa_decode_paged,

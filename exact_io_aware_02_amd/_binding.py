@@ -73,6 +73,8 @@ def _load():
         "fa_bwd_workspace_bytes": (Z, [I, I, I]),
         "fa_decode_ex": (I, [P, P, P, P, P, I, I, P, I, I, I, F, P, Z, P]),
         "fa_decode_workspace_bytes": (Z, [I, I, I, I]),
+        "fa_decode_fused": (I, [P, P, P, P, P, I, I, P, I, I, I, F, P, Z, P]),
+        "fa_decode_fused_workspace_bytes": (Z, [I, I, I, I]),
         "fa_decode_noalloc": (I, [P, P, P, P, P, I, I, P, I, I, I, F, P]),
         "fa_decode_noalloc_scratch_bytes": (Z, []),
         "fa_decode_paged": (I, [P, P, P, P, P, I, I, P, I, P, I, I, I, I, F, P, Z, P]),
@@ -107,6 +109,8 @@ EXPORTED = (
     "fa_decode",
     "fa_decode_ex",
     "fa_decode_workspace_bytes",
+    "fa_decode_fused",
+    "fa_decode_fused_workspace_bytes",
     "fa_decode_noalloc",
     "fa_decode_noalloc_scratch_bytes",
     "fa_decode_paged",
@@ -300,6 +304,31 @@ def fa_decode_ex(q, Kcache, Vcache, o, Lkv, workspace, lse_out=None, kv_seq_capa
     _check(lib.fa_decode_ex(_ptr(q), _ptr(Kcache), _ptr(Vcache), _ptr(o), _ptr(lse_out), B, H,
                             _ptr(Lkv), int(kv_seq_capacity), d, int(num_splits), float(scale),
                             _ptr(workspace), nbytes, _stream_ptr(stream)))
+    return o, lse_out
+
+
+def fa_decode_fused_workspace_bytes(B, H, d, num_splits=0):
+    return lib.fa_decode_fused_workspace_bytes(int(B), int(H), int(d), int(num_splits))
+
+
+def fa_decode_fused(q, Kcache, Vcache, o, Lkv, workspace, lse_out=None, kv_seq_capacity=0, num_splits=0,
+                    scale=None, stream=None):
+    """fa_decode_ex in one launch (the last split workgroup of each (b, h)
+    merges).  workspace: a device tensor of at least
+    fa_decode_fused_workspace_bytes(...) bytes whose counters (its last
+    B * H int32 after the partials) are zero before the first call, e.g.
+    torch.zeros; every completed call leaves them zero."""
+    import torch
+
+    B, H, d = _decode_shapes(q, Kcache, Vcache, o, Lkv)
+    if lse_out is not None:
+        _expect(lse_out, torch.float32, (B, H), "lse_out")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(lib.fa_decode_fused(_ptr(q), _ptr(Kcache), _ptr(Vcache), _ptr(o), _ptr(lse_out), B, H, _ptr(Lkv),
+                               int(kv_seq_capacity), d, int(num_splits), float(scale), _ptr(workspace), nbytes,
+                               _stream_ptr(stream)))
     return o, lse_out
 
 

@@ -178,7 +178,7 @@ struct PagedArgs {
 
 int decode_common(const void* q, const void* Kc, const void* Vc, void* o, float* lse, int B, int H,
                   const int32_t* Lkv, int cap, int d, int S, float scale, void* ws, hipStream_t st,
-                  const PagedArgs& pg = PagedArgs()) {
+                  const PagedArgs& pg = PagedArgs(), int* counters = nullptr) {
   fa::DecodeArgs a;
   a.q = q;
   a.K = Kc;
@@ -198,6 +198,7 @@ int decode_common(const void* q, const void* Kc, const void* Vc, void* o, float*
   a.max_blocks = pg.max_blocks;
   a.log2_bs = pg.log2_bs;
   a.num_blocks = pg.num_blocks;
+  a.counters = counters;
   hipError_t e = fa::launch_decode(a, d, st);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   return ok();
@@ -463,6 +464,47 @@ int fa_decode_ex(const void* q, const void* Kcache, const void* Vcache, void* o,
     return fail(FA_ERR_INVALID_ARG, "workspace overlaps q or o");
   return decode_common(q, Kcache, Vcache, o, lse_out, B, H, Lkv, kv_seq_capacity, d, S, scale,
                        workspace, static_cast<hipStream_t>(stream));
+}
+
+// The one-launch decode's workspace: a fixed region of kFusedCounters int32
+// counters first (so that a workspace reused for another shape finds its
+// counters where the previous call left them, at zero), then the partials.
+constexpr int64_t kFusedCounters = 65536;
+constexpr size_t kFusedCounterBytes = kFusedCounters * sizeof(int);
+
+size_t fa_decode_fused_workspace_bytes(int B, int H, int d, int num_splits) {
+  if ((int64_t)B * H > kFusedCounters) return 0;
+  const size_t parts = fa_decode_workspace_bytes(B, H, d, num_splits);
+  return parts ? kFusedCounterBytes + parts : 0;
+}
+
+int fa_decode_fused(const void* q, const void* Kcache, const void* Vcache, void* o, float* lse_out,
+                    int B, int H, const int32_t* Lkv, int kv_seq_capacity, int d, int num_splits,
+                    float scale, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_decode(q, Kcache, Vcache, o, lse_out, B, H, Lkv, kv_seq_capacity, d, num_splits, scale);
+  if (st != FA_OK) return st;
+  if (!workspace) return fail(FA_ERR_WORKSPACE, "null workspace");
+  if (!aligned(workspace, 256)) return fail(FA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if ((int64_t)B * H > kFusedCounters)
+    return fail(FA_ERR_UNSUPPORTED, "B * H = %lld exceeds the %lld counters of the one-launch decode",
+                (long long)B * H, (long long)kFusedCounters);
+  int S = num_splits;
+  if (S == 0) {
+    int cus = 0;
+    if ((st = cu_count(&cus)) != FA_OK) return st;
+    S = auto_splits(B, H, cus);
+  }
+  const size_t need = kFusedCounterBytes + ws_bytes(B, H, d, S);
+  if (workspace_bytes < need)
+    return fail(FA_ERR_WORKSPACE, "workspace of %zu bytes is too small (%zu needed)", workspace_bytes, need);
+  if (overlap(workspace, need, o, (size_t)B * H * d * 2) || overlap(workspace, need, q, (size_t)B * H * d * 2))
+    return fail(FA_ERR_INVALID_ARG, "workspace overlaps q or o");
+  if (lse_out && overlap(workspace, need, lse_out, (size_t)B * H * sizeof(float)))
+    return fail(FA_ERR_INVALID_ARG, "workspace overlaps lse_out");
+  int* counters = static_cast<int*>(workspace);
+  return decode_common(q, Kcache, Vcache, o, lse_out, B, H, Lkv, kv_seq_capacity, d, S, scale,
+                       static_cast<char*>(workspace) + kFusedCounterBytes, static_cast<hipStream_t>(stream),
+                       PagedArgs(), counters);
 }
 
 size_t fa_decode_noalloc_scratch_bytes(void) { return kNoAllocScratchBytes; }

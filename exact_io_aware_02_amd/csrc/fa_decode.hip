@@ -27,6 +27,17 @@
 // Combine kernel, grid (H, B): M = max_k lse_k, w_k = e^{lse_k - M},
 // o = sum_k w_k O^(k) / sum_k w_k, lse = M + ln sum_k w_k.
 //
+// One launch (fa_decode_fused): the split kernel itself merges.  Each split
+// workgroup publishes its partial and counts itself in a per-(b, h) counter;
+// the workgroup that brings the count to S merges the S partials with the
+// combine kernel's arithmetic (so the results are bit-identical) and resets
+// the counter.  The merge order is free ("Prefill and decode"), so which
+// workgroup is last does not matter.  Publishing to a workgroup that may run
+// on another XCD takes an agent-scope release: one wavefront writes the
+// partial and performs the release with the counting atomic (so the ordering
+// is within one instruction stream), and the last workgroup acquires before
+// it reads.
+//
 // Paged caches ("CMU 10-423 Lecture 18" notes, section 7.3): the cache is a
 // pool of blocks of 2^log2_bs tokens, [num_blocks, H, block_size, d], and a
 // block table maps each sequence's logical block to a physical one.  The
@@ -73,12 +84,74 @@ __device__ __forceinline__ void bf16x8_to_f32(const u32x4_t v, float* f) {
   }
 }
 
-template <int D, bool PAGED>
+constexpr int kCombineThreads = 256;
+constexpr int kMaxSplits = 4096;  // the host rejects larger split counts
+
+// Block-wide max / sum over kCombineThreads threads (4 wavefronts).
+template <bool MAX>
+__device__ __forceinline__ float block_reduce(float x, float* red) {
+  for (int off = 32; off > 0; off >>= 1) {
+    const float y = __shfl_xor(x, off);
+    x = MAX ? fmaxf(x, y) : x + y;
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __syncthreads();
+  if (lane == 0) red[wave] = x;
+  __syncthreads();
+  x = red[0];
+  for (int w = 1; w < kCombineThreads / 64; ++w) x = MAX ? fmaxf(x, red[w]) : x + red[w];
+  return x;
+}
+
+// The merge of the S partials of (b, h) = bh by one workgroup of
+// kCombineThreads threads: M = max_k lse_k, w_k = e^{lse_k - M},
+// o = sum_k w_k O^(k) / sum_k w_k, lse = M + ln sum_k w_k.  w (kMaxSplits
+// floats), red and osum are LDS.  The partials are read with plain loads
+// (not through the read-only path): in one launch they were written by
+// other workgroups of the same kernel.
+template <int D>
+__device__ __forceinline__ void combine_partials(const float* part_o, const float* part_lse, __bf16* og,
+                                                 float* lse_out, size_t bh, int S, float* w, float* red,
+                                                 float* osum) {
+  const int t = threadIdx.x;
+  const size_t base = bh * S;
+  float M = -INFINITY;
+  for (int k = t; k < S; k += kCombineThreads) M = fmaxf(M, part_lse[base + k]);
+  M = block_reduce<true>(M, red);
+  float sw = 0.f;
+  for (int k = t; k < S; k += kCombineThreads) {
+    const float lk = part_lse[base + k];
+    const float wk = (M == -INFINITY || lk == -INFINITY) ? 0.f : __expf(lk - M);
+    w[k] = wk;
+    sw += wk;
+  }
+  sw = block_reduce<false>(sw, red);  // its barriers also publish w[]
+
+  // column t % D, partials k = t / D, t / D + 256 / D, ...
+  constexpr int kGroups = kCombineThreads / D;
+  const int col = t % D;
+  float o = 0.f;
+  for (int k = t / D; k < S; k += kGroups) o = __builtin_fmaf(w[k], part_o[(base + k) * D + col], o);
+  osum[t] = o;
+  __syncthreads();
+  if (t < D) {
+    float acc = osum[t];
+#pragma unroll
+    for (int gi = 1; gi < kGroups; ++gi) acc += osum[t + gi * D];
+    og[bh * D + t] = (__bf16)(sw > 0.f ? acc / sw : 0.f);
+    if (lse_out != nullptr && t == 0) lse_out[bh] = (M == -INFINITY) ? -INFINITY : M + __logf(sw);
+  }
+}
+
+// FUSED: publish the partial, count the split in counters[b * H + h], and
+// merge if this workgroup completes the count (og, lse_out: the outputs).
+template <int D, bool PAGED, bool FUSED = false>
 __global__ __launch_bounds__(kThreads) void decode_split_kernel(
     const __bf16* __restrict__ qg, const __bf16* __restrict__ Kg, const __bf16* __restrict__ Vg,
-    const int32_t* __restrict__ Lkv, float* __restrict__ part_o, float* __restrict__ part_lse,
+    const int32_t* __restrict__ Lkv, float* part_o, float* part_lse,
     int H, int S, int capacity, float scale, const int32_t* __restrict__ table, int max_blocks,
-    int log2_bs, int num_blocks) {
+    int log2_bs, int num_blocks, int* counters = nullptr, __bf16* og = nullptr, float* lse_out = nullptr) {
+  static_assert(!FUSED || kThreads == kCombineThreads, "the merge runs on the split workgroup");
   constexpr int CPR = D / 8;        // lanes per key row (16-byte chunks per row)
   constexpr int KPI = 64 / CPR;     // key rows per wavefront load instruction
   constexpr int KPB = KPI * kUnroll;  // keys per wavefront block
@@ -124,11 +197,13 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
   const int start = split * chunk;
   const int end = min(len, start + chunk);
   const size_t out = ((size_t)b * H + h) * S + split;
-  if (start >= end) {
+  if (!FUSED && start >= end) {
     for (int e = tid; e < D; e += kThreads) part_o[out * D + e] = 0.f;
     if (tid == 0) part_lse[out] = -INFINITY;
     return;
   }
+  // (fused: an empty chunk reads nothing and publishes the partial (0, -inf)
+  // like any other, so that it is counted)
 
   // query slice, pre-scaled into the base-2 domain
   float qv[8];
@@ -145,7 +220,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
 
   // paged: this chunk's physical block ids (the host bounds their count)
   const int e_first = start >> log2_bs;
-  if (PAGED) {
+  if (PAGED && start < end) {
     const int e_last = (end - 1) >> log2_bs;
     for (int e = e_first + tid; e <= e_last; e += kThreads) ids[e - e_first] = table[(size_t)b * max_blocks + e];
     __syncthreads();
@@ -158,7 +233,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
 
   // blocks of KPB keys, dealt round-robin to the wavefronts; the next block
   // of this wavefront is loaded while the current one is consumed
-  const int n_blocks = (end - start + KPB - 1) / KPB;
+  const int n_blocks = start < end ? (end - start + KPB - 1) / KPB : 0;
 
   // bit u of `valid` is cleared when load u's block id is out of range
   // (paged only); such keys score -inf
@@ -268,32 +343,43 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
   }
   // a chunk whose keys were all skipped (paged, invalid ids) is empty
   const float inv = L2 > 0.f ? 1.f / L2 : 0.f;
-  for (int e = tid; e < D; e += kThreads) {
-    float o = 0.f;
+  if constexpr (!FUSED) {
+    for (int e = tid; e < D; e += kThreads) {
+      float o = 0.f;
 #pragma unroll
-    for (int w = 0; w < kDecWaves; ++w) o += f[w] * wacc[w][e];
-    part_o[out * D + e] = o * inv;
+      for (int w = 0; w < kDecWaves; ++w) o += f[w] * wacc[w][e];
+      part_o[out * D + e] = o * inv;
+    }
+    if (tid == 0) part_lse[out] = L2 > 0.f ? (M + __log2f(L2)) * kLn2 : -INFINITY;
+  } else {
+    __shared__ int last;
+    __shared__ float cw[kMaxSplits];
+    __shared__ float cred[kCombineThreads / 64];
+    __shared__ float cosum[kCombineThreads];
+    const size_t bh = (size_t)b * H + h;
+    if (wave == 0) {
+      // the same values as the two-launch path, written by this wavefront
+      // alone, which then releases them with the count
+      for (int e = lane; e < D; e += 64) {
+        float o = 0.f;
+#pragma unroll
+        for (int w = 0; w < kDecWaves; ++w) o += f[w] * wacc[w][e];
+        part_o[out * D + e] = o * inv;
+      }
+      if (lane == 0) {
+        part_lse[out] = L2 > 0.f ? (M + __log2f(L2)) * kLn2 : -INFINITY;
+        const int prev = __hip_atomic_fetch_add(&counters[bh], 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        last = prev == S - 1;
+      }
+    }
+    __syncthreads();
+    if (!last) return;
+    // every partial of (b, h) is published: acquire, reset the counter for
+    // the next call, merge
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    if (tid == 0) __hip_atomic_store(&counters[bh], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    combine_partials<D>(part_o, part_lse, og, lse_out, bh, S, cw, cred, cosum);
   }
-  if (tid == 0) part_lse[out] = L2 > 0.f ? (M + __log2f(L2)) * kLn2 : -INFINITY;
-}
-
-constexpr int kCombineThreads = 256;
-constexpr int kMaxSplits = 4096;  // the host rejects larger split counts
-
-// Block-wide max / sum over kCombineThreads threads (4 wavefronts).
-template <bool MAX>
-__device__ __forceinline__ float block_reduce(float x, float* red) {
-  for (int off = 32; off > 0; off >>= 1) {
-    const float y = __shfl_xor(x, off);
-    x = MAX ? fmaxf(x, y) : x + y;
-  }
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  __syncthreads();
-  if (lane == 0) red[wave] = x;
-  __syncthreads();
-  x = red[0];
-  for (int w = 1; w < kCombineThreads / 64; ++w) x = MAX ? fmaxf(x, red[w]) : x + red[w];
-  return x;
 }
 
 template <int D>
@@ -303,40 +389,19 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(
   __shared__ float w[kMaxSplits];
   __shared__ float red[kCombineThreads / 64];
   __shared__ float osum[kCombineThreads];
-  const int h = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
-  const size_t bh = (size_t)b * H + h;
-  const size_t base = bh * S;
-
-  float M = -INFINITY;
-  for (int k = t; k < S; k += kCombineThreads) M = fmaxf(M, part_lse[base + k]);
-  M = block_reduce<true>(M, red);
-  float sw = 0.f;
-  for (int k = t; k < S; k += kCombineThreads) {
-    const float lk = part_lse[base + k];
-    const float wk = (M == -INFINITY || lk == -INFINITY) ? 0.f : __expf(lk - M);
-    w[k] = wk;
-    sw += wk;
-  }
-  sw = block_reduce<false>(sw, red);  // its barriers also publish w[]
-
-  // column t % D, partials k = t / D, t / D + 256 / D, ...
-  constexpr int kGroups = kCombineThreads / D;
-  const int col = t % D;
-  float o = 0.f;
-  for (int k = t / D; k < S; k += kGroups) o = __builtin_fmaf(w[k], part_o[(base + k) * D + col], o);
-  osum[t] = o;
-  __syncthreads();
-  if (t < D) {
-    float acc = osum[t];
-#pragma unroll
-    for (int gi = 1; gi < kGroups; ++gi) acc += osum[t + gi * D];
-    og[bh * D + t] = (__bf16)(sw > 0.f ? acc / sw : 0.f);
-    if (lse_out != nullptr && t == 0) lse_out[bh] = (M == -INFINITY) ? -INFINITY : M + __logf(sw);
-  }
+  const int h = blockIdx.x, b = blockIdx.y;
+  combine_partials<D>(part_o, part_lse, og, lse_out, (size_t)b * H + h, S, w, red, osum);
 }
 
 template <int D>
 hipError_t launch(const DecodeArgs& a, hipStream_t stream) {
+  if (a.counters != nullptr) {
+    hipLaunchKernelGGL((decode_split_kernel<D, false, true>), dim3(a.S, a.H, a.B), dim3(kThreads), 0, stream,
+                       static_cast<const __bf16*>(a.q), static_cast<const __bf16*>(a.K),
+                       static_cast<const __bf16*>(a.V), a.Lkv, a.part_o, a.part_lse, a.H, a.S, a.capacity,
+                       a.scale, nullptr, 0, 0, 0, a.counters, static_cast<__bf16*>(a.o), a.lse_out);
+    return hipGetLastError();
+  }
   if (a.table != nullptr)
     hipLaunchKernelGGL((decode_split_kernel<D, true>), dim3(a.S, a.H, a.B), dim3(kThreads), 0, stream,
                        static_cast<const __bf16*>(a.q), static_cast<const __bf16*>(a.K),

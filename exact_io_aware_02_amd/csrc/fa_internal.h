@@ -100,6 +100,8 @@ struct DecodeArgs {
   // paged cache (table != nullptr): K/V are pools [num_blocks, H, 2^log2_bs, d]
   const int32_t* table = nullptr;  // [B, max_blocks]
   int max_blocks = 0, log2_bs = 0, num_blocks = 0;
+  // one launch: per-(b, h) counters [B, H], zero on entry and on exit
+  int* counters = nullptr;
 };
 
 // bf16 prefill with d = 128 runs the 64-rows-per-wavefront kernel (4

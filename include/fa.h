@@ -200,6 +200,36 @@ int fa_decode_ex(const void* q, const void* Kcache, const void* Vcache, void* o,
                  void* stream);
 
 /*
+ * fa_decode_fused -- fa_decode_ex in one launch: the last split workgroup of
+ * each (b, h) to finish performs the log-sum-exp merge (the airsota
+ * Flash-Decoding card, section 3, steps 1-3, with step 3 moved into the
+ * kernel of steps 1-2; "Infra: Flash Attention", "Prefill and decode": the
+ * merge order is free).
+ *   q, Kcache, Vcache, o, lse_out, Lkv, kv_seq_capacity, num_splits, scale :
+ *             as in fa_decode_ex
+ *   B * H   : at most 65536 (FA_ERR_UNSUPPORTED above)
+ *   workspace : caller-owned device memory of at least
+ *             fa_decode_fused_workspace_bytes(B, H, d, num_splits) bytes,
+ *             256-byte aligned: 65536 int32 counters (256 KiB), then the
+ *             split partials.  The counters must be zero before the first
+ *             call (for example a zero-filled allocation); each call that
+ *             completes leaves them zero again, so the workspace can be
+ *             reused call after call, for any shape that fits it.  Calls
+ *             that may run concurrently must not share one.
+ * Results are bit-identical to fa_decode_ex with the same arguments.
+ * Publishing a partial to a workgroup that may run on another XCD needs an
+ * agent-scope release per split workgroup, which on MI355X costs more than
+ * the second launch it saves: fa_decode_ex is the faster path.
+ * Allocates nothing.  Errors: as fa_decode_ex.
+ */
+int fa_decode_fused(const void* q, const void* Kcache, const void* Vcache, void* o, float* lse_out,
+                    int B, int H, const int32_t* Lkv, int kv_seq_capacity, int d, int num_splits,
+                    float scale, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes fa_decode_fused needs (0 for invalid arguments). */
+size_t fa_decode_fused_workspace_bytes(int B, int H, int d, int num_splits);
+
+/*
  * fa_decode_noalloc -- fa_decode_ex without a workspace argument and without
  * any allocation, for callers that cannot allocate device memory (code under
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).

@@ -357,3 +357,38 @@ def test_exp2_poly_share_is_validated():
         assert "0, 4, 8 or 16" in fa.last_error()
     finally:
         lib.fa_set_fwd_exp2_poly(0)
+
+
+def test_decode_fused_rejects_bad_workspace_and_arguments():
+    """The one-launch decode validates like fa_decode_ex; its workspace puts a
+    fixed region of 65536 int32 counters before the partials, and B * H above
+    65536 is unsupported."""
+    fa = _fa()
+    lib = fa.lib
+    args = (A, 2 * A, 3 * A, 4 * A, None, 2, 4, 5 * A)
+    parts = fa.fa_decode_workspace_bytes(2, 4, 128, 8)
+    need = fa.fa_decode_fused_workspace_bytes(2, 4, 128, 8)
+    assert need == parts + (1 << 18)
+    assert fa.fa_decode_fused_workspace_bytes(3, 100, 64, 7) == fa.fa_decode_workspace_bytes(3, 100, 64, 7) + (1 << 18)
+    assert fa.fa_decode_fused_workspace_bytes(0, 4, 128, 8) == 0
+    assert fa.fa_decode_fused_workspace_bytes(2, 4, 100, 8) == 0
+    assert fa.fa_decode_fused_workspace_bytes(257, 256, 128, 1) == 0
+    assert fa.fa_decode_fused_workspace_bytes(256, 256, 128, 1) > 0
+    G = 1 << 30  # addresses far enough apart for B * H = 65792 rows of q and o
+    assert lib.fa_decode_fused(G, 2 * G, 3 * G, 4 * G, None, 257, 256, 5 * G, 0, 128, 1, ctypes.c_float(0.1),
+                               6 * G, 1 << 30, None) == -2
+    assert "65536" in fa.last_error()
+    assert lib.fa_decode_fused(*args, -1, 128, 8, ctypes.c_float(0.1), 6 * A, need, None) == -1
+    assert lib.fa_decode_fused(*args, 0, 128, 8, ctypes.c_float(0.0), 6 * A, need, None) == -1
+    assert lib.fa_decode_fused(*args, 0, 100, 8, ctypes.c_float(0.1), 6 * A, need, None) == -2
+    assert lib.fa_decode_fused(*args, 0, 128, 8, ctypes.c_float(0.1), None, need, None) == -5
+    assert lib.fa_decode_fused(*args, 0, 128, 8, ctypes.c_float(0.1), 6 * A + 16, need, None) == -5
+    # room for the partials but not the counters
+    assert lib.fa_decode_fused(*args, 0, 128, 8, ctypes.c_float(0.1), 6 * A, parts, None) == -5
+    assert "too small" in fa.last_error()
+    # workspace over o (4 * A, 2 * 4 * 128 bf16) or over lse_out
+    assert lib.fa_decode_fused(*args, 0, 128, 8, ctypes.c_float(0.1), 4 * A - 256, need, None) == -1
+    assert "overlaps" in fa.last_error()
+    argsl = (A, 2 * A, 3 * A, 4 * A, 8 * A + 512, 2, 4, 5 * A)
+    assert lib.fa_decode_fused(*argsl, 0, 128, 8, ctypes.c_float(0.1), 8 * A, need, None) == -1
+    assert "lse_out" in fa.last_error()
