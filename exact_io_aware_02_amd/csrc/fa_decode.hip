@@ -35,8 +35,8 @@
 // workgroup is last does not matter.  Publishing to a workgroup that may run
 // on another XCD takes an agent-scope release: one wavefront writes the
 // partial and performs the release with the counting atomic (so the ordering
-// is within one instruction stream), and the last workgroup acquires before
-// it reads.
+// is within one instruction stream); only the last workgroup acquires,
+// before it reads.
 //
 // Paged caches ("CMU 10-423 Lecture 18" notes, section 7.3): the cache is a
 // pool of blocks of 2^log2_bs tokens, [num_blocks, H, block_size, d], and a
@@ -368,14 +368,19 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
       }
       if (lane == 0) {
         part_lse[out] = L2 > 0.f ? (M + __log2f(L2)) * kLn2 : -INFINITY;
-        const int prev = __hip_atomic_fetch_add(&counters[bh], 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        // release only: the workgroups that are not last need no acquire
+        const int prev = __hip_atomic_fetch_add(&counters[bh], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
         last = prev == S - 1;
+        // the last one acquires here: its atomic read the value of the
+        // release sequence of every other split's count
+        if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
       }
     }
     __syncthreads();
     if (!last) return;
-    // every partial of (b, h) is published: acquire, reset the counter for
-    // the next call, merge
+    // every partial of (b, h) is published: acquire (in every thread, after
+    // the barrier that orders them after thread 0's acquire), reset the
+    // counter for the next call, merge
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     if (tid == 0) __hip_atomic_store(&counters[bh], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     combine_partials<D>(part_o, part_lse, og, lse_out, bh, S, cw, cred, cosum);
