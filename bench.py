@@ -402,6 +402,7 @@ def main():
         result["causal_4k"] = {
             "value": round(tf_c, 2), "unit": "TFLOP/s", "ms_per_launch": round(ms_c, 5),
             "frac_of_peak": round(tf_c / PEAK_BF16_TFLOPS, 4),
+            "frac_of_measured": round(tf_c / ceil["mfma_bf16"]["value"], 4),
             "flops_algorithmic": alg, "flops_executed_tiles": executed,
         }
         log(f"causal_4k {ms_c:.4f} ms -> {tf_c:.1f} TFLOP/s")
