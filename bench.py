@@ -188,7 +188,8 @@ def measured_ceilings(torch, fa, cus):
       * fa_probe_mfma_bf16: 2 workgroups of 4 wavefronts per compute unit,
         each wavefront 16384 rounds of 4 independent 32x32x16 bf16 MFMAs;
         also the shader clock its wavefronts ran at (s_memtime cycles over
-        s_memrealtime ticks);
+        s_memrealtime ticks); and fa_probe_mfma_bf16_mixed, the same loop on
+        pseudo-random operands that differ between consecutive products;
       * fa_probe_hbm_read: one read of a 4 GiB buffer (16 times the last
         level cache), 64 workgroups of 256 threads per compute unit."""
     out = {}
@@ -202,6 +203,13 @@ def measured_ceilings(torch, fa, cus):
     out["mfma_bf16"] = {"value": round(flop / (ms * 1e-3) / 1e12, 1), "unit": "TFLOP/s",
                         "kernel": "fa_probe_mfma_bf16", "ms_per_launch": round(ms, 4),
                         "clock_ghz": round(clk, 3), "workgroups": wg, "iters": iters}
+    # the same loop on operands that change from product to product
+    ms = _timed(lambda i: fa.fa_probe_mfma_bf16_mixed(wg, iters, sink, stamps, seed=i + 1), 5, 3, torch)
+    st = stamps.cpu().double()
+    clk = (st[:, 0] / (st[:, 1] / 1e8)).median().item() / 1e9
+    out["mfma_bf16_mixed"] = {"value": round(flop / (ms * 1e-3) / 1e12, 1), "unit": "TFLOP/s",
+                              "kernel": "fa_probe_mfma_bf16_mixed", "ms_per_launch": round(ms, 4),
+                              "clock_ghz": round(clk, 3), "workgroups": wg, "iters": iters}
     del sink, stamps
     nbytes = 4 << 30
     buf = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
@@ -373,6 +381,8 @@ def main():
     log(f"ceilings {ceil}")
     result["roofline"]["measured_ceiling"] = ceil["mfma_bf16"]
     result["roofline"]["frac_of_measured"] = round(tflops / ceil["mfma_bf16"]["value"], 4)
+    result["roofline"]["measured_ceiling_mixed_operands"] = ceil["mfma_bf16_mixed"]
+    result["roofline"]["frac_of_measured_mixed"] = round(tflops / ceil["mfma_bf16_mixed"]["value"], 4)
     result["decode"]["roofline"]["measured_ceiling"] = ceil["hbm_read"]
     result["decode"]["roofline"]["frac_of_measured"] = round(dec_gbs / ceil["hbm_read"]["value"], 4)
 

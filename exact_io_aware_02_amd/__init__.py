@@ -36,6 +36,7 @@ from ._binding import (  # noqa: F401
     fa_set_fwd_exp2_poly,
     fa_probe_hbm_read,
     fa_probe_mfma_bf16,
+    fa_probe_mfma_bf16_mixed,
     fa_release_workspace,
     last_error,
     lib,

@@ -85,6 +85,7 @@ def _load():
         "fa_release_workspace": (I, []),
         "fa_probe_hbm_read": (I, [P, Z, I, P, P]),
         "fa_probe_mfma_bf16": (I, [I, I, P, P, P]),
+        "fa_probe_mfma_bf16_mixed": (I, [I, I, ctypes.c_uint32, P, P, P]),
         "fa_status_string": (ctypes.c_char_p, [I]),
         "fa_last_error": (ctypes.c_char_p, []),
         "fa_version": (I, []),
@@ -121,6 +122,7 @@ EXPORTED = (
     "fa_release_workspace",
     "fa_probe_hbm_read",
     "fa_probe_mfma_bf16",
+    "fa_probe_mfma_bf16_mixed",
     "fa_status_string",
     "fa_last_error",
     "fa_version",
@@ -419,3 +421,15 @@ def fa_probe_mfma_bf16(workgroups, iters, sink, stamps=None, stream=None):
     if stamps is not None:
         _expect(stamps, torch.int64, (workgroups, 2), "stamps")
     _check(lib.fa_probe_mfma_bf16(int(workgroups), int(iters), _ptr(sink), _ptr(stamps), _stream_ptr(stream)))
+
+
+def fa_probe_mfma_bf16_mixed(workgroups, iters, sink, stamps=None, seed=1, stream=None):
+    """fa_probe_mfma_bf16 with pseudo-random operands that differ between
+    consecutive products (seeded by `seed`)."""
+    import torch
+
+    _expect(sink, torch.float32, (workgroups * 256,), "sink")
+    if stamps is not None:
+        _expect(stamps, torch.int64, (workgroups, 2), "stamps")
+    _check(lib.fa_probe_mfma_bf16_mixed(int(workgroups), int(iters), int(seed) & 0xFFFFFFFF, _ptr(sink),
+                                        _ptr(stamps), _stream_ptr(stream)))

@@ -615,7 +615,7 @@ int fa_probe_hbm_read(const void* buf, size_t bytes, int workgroups, uint32_t* s
   return e == hipSuccess ? ok() : hip_fail(e, "probe launch");
 }
 
-int fa_probe_mfma_bf16(int workgroups, int iters, float* sink, uint64_t* stamps, void* stream) {
+static int check_probe_mfma(int workgroups, int iters, const float* sink, const uint64_t* stamps) {
   if (!sink) return fail(FA_ERR_INVALID_ARG, "null sink");
   if (!aligned(sink, 4) || (stamps && !aligned(stamps, 8)))
     return fail(FA_ERR_INVALID_ARG, "sink must be 4-byte and stamps 8-byte aligned");
@@ -624,7 +624,21 @@ int fa_probe_mfma_bf16(int workgroups, int iters, float* sink, uint64_t* stamps,
   if (iters < 1 || iters > (1 << 24)) return fail(FA_ERR_INVALID_ARG, "iters must be in [1, 16777216] (got %d)", iters);
   if (stamps && overlap(sink, (size_t)workgroups * 256 * 4, stamps, (size_t)workgroups * 16))
     return fail(FA_ERR_INVALID_ARG, "stamps overlaps sink");
+  return FA_OK;
+}
+
+int fa_probe_mfma_bf16(int workgroups, int iters, float* sink, uint64_t* stamps, void* stream) {
+  int st = check_probe_mfma(workgroups, iters, sink, stamps);
+  if (st != FA_OK) return st;
   hipError_t e = fa::launch_probe_mfma_bf16(workgroups, iters, sink, stamps, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ok() : hip_fail(e, "probe launch");
+}
+
+int fa_probe_mfma_bf16_mixed(int workgroups, int iters, uint32_t seed, float* sink, uint64_t* stamps, void* stream) {
+  int st = check_probe_mfma(workgroups, iters, sink, stamps);
+  if (st != FA_OK) return st;
+  hipError_t e =
+      fa::launch_probe_mfma_bf16_mixed(workgroups, iters, seed, sink, stamps, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ok() : hip_fail(e, "probe launch");
 }
 

@@ -120,6 +120,8 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, int d, hipStream_t stream);
 hipError_t launch_probe_hbm_read(const void* buf, size_t bytes, int workgroups, uint32_t* sink,
                                  hipStream_t stream);
 hipError_t launch_probe_mfma_bf16(int workgroups, int iters, float* sink, uint64_t* stamps, hipStream_t stream);
+hipError_t launch_probe_mfma_bf16_mixed(int workgroups, int iters, uint32_t seed, float* sink, uint64_t* stamps,
+                                        hipStream_t stream);
 
 // Host-side tile bookkeeping used by both the planner and the launcher.
 __host__ __device__ inline int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }

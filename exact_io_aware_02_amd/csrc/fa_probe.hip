@@ -79,7 +79,58 @@ __global__ __launch_bounds__(256) void probe_mfma_bf16_kernel(int iters, float* 
   }
 }
 
+// The same loop with operands that change from one product to the next,
+// like the attention kernels' fragments: each of the four chains has its own
+// A and B, filled from an integer hash of (seed, workgroup, lane, chain,
+// element) with values in [-2, 2), and the chains take turns.  Constant
+// operands (above) leave the matrix datapath almost idle between products,
+// which lets the clock run higher than under real data.
+__device__ __forceinline__ uint32_t probe_hash(uint32_t x) {
+  x ^= x >> 16;
+  x *= 0x7feb352du;
+  x ^= x >> 15;
+  x *= 0x846ca68bu;
+  x ^= x >> 16;
+  return x;
+}
+
+__global__ __launch_bounds__(256) void probe_mfma_bf16_mixed_kernel(int iters, uint32_t seed, float* __restrict__ sink,
+                                                                     uint64_t* __restrict__ stamps) {
+  const int lane = threadIdx.x & 63;
+  bf16x8 a[4], b[4];
+  for (int c = 0; c < 4; ++c)
+    for (int k = 0; k < 8; ++k) {
+      const uint32_t base = seed * 0x9e3779b9u ^ ((blockIdx.x * 256 + threadIdx.x) * 64 + c * 16 + k);
+      a[c][k] = (__bf16)((float)(probe_hash(2 * base) >> 8) * 0x1p-22f - 2.f);
+      b[c][k] = (__bf16)((float)(probe_hash(2 * base + 1) >> 8) * 0x1p-22f - 2.f);
+    }
+  f32x16 c0 = {}, c1 = {}, c2 = {}, c3 = {};
+  const uint64_t t0 = __builtin_amdgcn_s_memtime();
+  const uint64_t r0 = __builtin_amdgcn_s_memrealtime();
+  for (int it = 0; it < iters; ++it) {
+    c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0], b[0], c0, 0, 0, 0);
+    c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1], b[1], c1, 0, 0, 0);
+    c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[2], b[2], c2, 0, 0, 0);
+    c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[3], b[3], c3, 0, 0, 0);
+  }
+  float s = 0.f;
+  for (int k = 0; k < 16; ++k) s += c0[k] + c1[k] + c2[k] + c3[k];
+  const uint64_t t1 = __builtin_amdgcn_s_memtime();
+  const uint64_t r1 = __builtin_amdgcn_s_memrealtime();
+  sink[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = s;
+  if (threadIdx.x == 0 && stamps) {
+    stamps[2 * blockIdx.x] = t1 - t0;
+    stamps[2 * blockIdx.x + 1] = r1 - r0;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_probe_mfma_bf16_mixed(int workgroups, int iters, uint32_t seed, float* sink, uint64_t* stamps,
+                                        hipStream_t stream) {
+  hipLaunchKernelGGL(probe_mfma_bf16_mixed_kernel, dim3(workgroups), dim3(256), 0, stream, iters, seed, sink, stamps);
+  return hipGetLastError();
+}
 
 hipError_t launch_probe_hbm_read(const void* buf, size_t bytes, int workgroups, uint32_t* sink, hipStream_t stream) {
   hipLaunchKernelGGL(probe_hbm_read_kernel, dim3(workgroups), dim3(256), 0, stream,

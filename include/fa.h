@@ -336,9 +336,19 @@ int fa_release_workspace(void);
  *           each workgroup, the shader-clock cycles and the 100 MHz
  *           constant-clock ticks its first wavefront spent in the loop
  *           (cycles / (ticks / 1e8) = the clock it ran at)
- * Both: errors FA_ERR_INVALID_ARG (checked before any HIP call), FA_ERR_HIP. */
+ *
+ * fa_probe_mfma_bf16_mixed: the same loop and arguments, but every chain has
+ * its own A and B operands, pseudo-random in [-2, 2) (an integer hash of
+ * seed, workgroup, lane, chain and element), so consecutive products read
+ * different data, as the attention kernels' products do.  Constant operands
+ * leave the matrix datapath nearly idle between products, which lets the
+ * clock run higher than real data does.
+ * All three: errors FA_ERR_INVALID_ARG (checked before any HIP call),
+ * FA_ERR_HIP. */
 int fa_probe_hbm_read(const void* buf, size_t bytes, int workgroups, uint32_t* sink, void* stream);
 int fa_probe_mfma_bf16(int workgroups, int iters, float* sink, uint64_t* stamps, void* stream);
+int fa_probe_mfma_bf16_mixed(int workgroups, int iters, uint32_t seed, float* sink, uint64_t* stamps,
+                             void* stream);
 
 /* Static description of a status code, and the thread-local message of the
  * last failing call on this thread ("" if none). */

@@ -338,6 +338,10 @@ def test_probes_reject_invalid_arguments():
     assert lib.fa_probe_mfma_bf16(4, 0, A, None, None) == -1
     assert lib.fa_probe_mfma_bf16(4, 10, A, A + 4, None) == -1           # stamps misaligned
     assert lib.fa_probe_mfma_bf16(4, 10, A, A + 8, None) == -1           # stamps inside sink
+    assert lib.fa_probe_mfma_bf16_mixed(4, 10, 1, None, None, None) == -1
+    assert lib.fa_probe_mfma_bf16_mixed(0, 10, 1, A, None, None) == -1
+    assert lib.fa_probe_mfma_bf16_mixed(4, 1 << 25, 1, A, None, None) == -1
+    assert lib.fa_probe_mfma_bf16_mixed(4, 10, 1, A, A + 8, None) == -1
 
 
 def test_exp2_poly_share_is_validated():

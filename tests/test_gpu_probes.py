@@ -79,3 +79,46 @@ def test_mfma_probe_products_and_clock():
     ghz = st[:, 0] / (st[:, 1] / 1e8) / 1e9
     print("[case] mfma probe clock GHz", ghz, flush=True)
     assert ((ghz > 0.3) & (ghz < 3.0)).all(), ghz
+
+
+def _hash(x):
+    x = x.astype(np.uint64) & 0xFFFFFFFF
+    x ^= x >> 16
+    x = (x * 0x7FEB352D) & 0xFFFFFFFF
+    x ^= x >> 15
+    x = (x * 0x846CA68B) & 0xFFFFFFFF
+    x ^= x >> 16
+    return x
+
+
+def test_mfma_mixed_probe_products():
+    """The mixed-operand probe: per wavefront the stored sums add up to iters
+    x the sum over its four chains of the 32x32 products of the operands the
+    kernel hashes (rebuilt here with the same integer hash, rounded to bf16),
+    and a different seed gives different operands."""
+    fa = _fa()
+    wg, iters, seed = 2, 3, 7
+    sink = torch.empty(wg * 256, dtype=torch.float32, device="cuda")
+    stamps = torch.zeros(wg, 2, dtype=torch.int64, device="cuda")
+    fa.fa_probe_mfma_bf16_mixed(wg, iters, sink, stamps, seed=seed)
+    torch.cuda.synchronize()
+    got = sink.cpu().double().numpy().reshape(-1, 64).sum(1)
+    want = []
+    for blk in range(wg):
+        for w in range(4):
+            tid = np.arange(64) + 64 * w
+            tot = 0.0
+            for c in range(4):
+                base = ((seed * 0x9E3779B9) & 0xFFFFFFFF) ^ (((blk * 256 + tid) * 64 + c * 16)[:, None] + np.arange(8))
+                ha = _hash((2 * base) & 0xFFFFFFFF)
+                hb = _hash((2 * base + 1) & 0xFFFFFFFF)
+                a = _bf16((ha >> 8).astype(np.float64) * 2.0 ** -22 - 2.0)
+                b = _bf16((hb >> 8).astype(np.float64) * 2.0 ** -22 - 2.0)
+                tot += sum(a[32 * h:32 * h + 32, k].sum() * b[32 * h:32 * h + 32, k].sum()
+                           for h in range(2) for k in range(8))
+            want.append(iters * tot)
+    want = np.array(want)
+    assert np.allclose(got, want, rtol=1e-3, atol=1e-2 * np.abs(want).max()), (got[:4], want[:4])
+    fa.fa_probe_mfma_bf16_mixed(wg, iters, sink, stamps, seed=seed + 1)
+    torch.cuda.synchronize()
+    assert not np.allclose(sink.cpu().double().numpy().reshape(-1, 64).sum(1), got)
