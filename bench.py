@@ -203,7 +203,7 @@ def measured_ceilings(torch, fa, cus):
     out["mfma_bf16"] = {"value": round(flop / (ms * 1e-3) / 1e12, 1), "unit": "TFLOP/s",
                         "kernel": "fa_probe_mfma_bf16", "ms_per_launch": round(ms, 4),
                         "clock_ghz": round(clk, 3), "workgroups": wg, "iters": iters}
-    # the same loop on operands that change from product to product
+    # the same loop on random operands that change from product to product
     ms = _timed(lambda i: fa.fa_probe_mfma_bf16_mixed(wg, iters, sink, stamps, seed=i + 1), 5, 3, torch)
     st = stamps.cpu().double()
     clk = (st[:, 0] / (st[:, 1] / 1e8)).median().item() / 1e9

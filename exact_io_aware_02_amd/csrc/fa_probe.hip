@@ -82,9 +82,11 @@ __global__ __launch_bounds__(256) void probe_mfma_bf16_kernel(int iters, float* 
 // The same loop with operands that change from one product to the next,
 // like the attention kernels' fragments: each of the four chains has its own
 // A and B, filled from an integer hash of (seed, workgroup, lane, chain,
-// element) with values in [-2, 2), and the chains take turns.  Constant
-// operands (above) leave the matrix datapath almost idle between products,
-// which lets the clock run higher than under real data.
+// element) with values in [-2, 2), and the chains take turns.  The loop
+// above multiplies small multiples of 0.001 and 0.002, many of them zero;
+// with random bf16 values held constant it runs within 4 % of this one, so
+// the operand values, more than their changing between products, set the
+// power the products draw and so the clock.
 __device__ __forceinline__ uint32_t probe_hash(uint32_t x) {
   x ^= x >> 16;
   x *= 0x7feb352du;

@@ -340,9 +340,11 @@ int fa_release_workspace(void);
  * fa_probe_mfma_bf16_mixed: the same loop and arguments, but every chain has
  * its own A and B operands, pseudo-random in [-2, 2) (an integer hash of
  * seed, workgroup, lane, chain and element), so consecutive products read
- * different data, as the attention kernels' products do.  Constant operands
- * leave the matrix datapath nearly idle between products, which lets the
- * clock run higher than real data does.
+ * different data, as the attention kernels' products do.  The constant loop
+ * multiplies small multiples of 0.001 and 0.002, many of them zero; with
+ * random bf16 values held constant it runs within 4 % of this loop: the
+ * operand values, more than their changing between products, set the power
+ * the products draw and so the clock.
  * All three: errors FA_ERR_INVALID_ARG (checked before any HIP call),
  * FA_ERR_HIP. */
 int fa_probe_hbm_read(const void* buf, size_t bytes, int workgroups, uint32_t* sink, void* stream);
